@@ -1,0 +1,224 @@
+/*
+ * zero_shard.h -- C ABI of the ZeRO-1/2 owner-shard step on MI355X (gfx950).
+ *
+ * The owner-shard step is the part of a ZeRO-1/2 data-parallel step that the
+ * owner of one partition of a flat parameter group runs after the backward
+ * pass:
+ *
+ *   1. layout   the group's tensors are flattened into one buffer, padded for
+ *               alignment and cut into N equal partitions, one per rank
+ *               (ZeRO-2 source walkthrough, discosf.com, sections 2.1 and 4.1);
+ *   2. reduce   the owner receives the sum of the N ranks' 16-bit gradients
+ *               for its partition (ZeRO 优化器, cookllm.com, "ZeRO Stage 1"
+ *               gradient sync; ZeRO-2 source walkthrough sections 4.2 and 三);
+ *   3. check    unscale by the loss scale, test for inf/NaN (an overflow skips
+ *               the step) and take the squared L2 norm for clipping (wmrh.cn
+ *               ZeRO article, section 3.1 fp16 block and section 3.3
+ *               gradient_clipping);
+ *   4. adamw    AdamW on the partition's fp32 master weights, m and v, then the
+ *               16-bit copy of the new weights (ZeRO-2 source walkthrough,
+ *               sections 4.1 step 3 and 4.3);
+ *   5. scaler   dynamic loss-scale update (wmrh.cn article, section 3.1).
+ *
+ * Conventions for every call:
+ *   - Buffers are flat arrays.  "device" pointers are HIP device memory owned
+ *     by the caller; "host" pointers are ordinary host memory owned by the
+ *     caller.  The library never allocates, frees or keeps a pointer after a
+ *     call returns, and keeps no state between calls.
+ *   - 16-bit data (gradients, the parameter copy) is passed as raw 16-bit
+ *     patterns; `dtype` says whether they are IEEE binary16 or bfloat16.
+ *   - Device calls are asynchronous and ordered on `stream` (0 = the null
+ *     stream).  None of them synchronises.  Any element offset is accepted;
+ *     pointers that share their alignment modulo 16 bytes take the 128-bit
+ *     vector path for everything but at most 7 leading and 7 trailing elements.
+ *   - Arguments are checked before anything is launched; a bad argument
+ *     returns ZERO_EINVAL (or ZERO_ERANGE for sizes that overflow) and
+ *     launches nothing.  A failed launch returns ZERO_EDEVICE.  No call
+ *     aborts, throws or prints.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum zero_status {
+    ZERO_OK = 0,
+    ZERO_EINVAL = -1,  /* bad argument: null pointer, negative size, unknown dtype ... */
+    ZERO_ERANGE = -2,  /* a size or offset overflows int64                              */
+    ZERO_EDEVICE = -3  /* a HIP launch failed                                           */
+};
+
+enum zero_dtype {
+    ZERO_FP16 = 1,     /* IEEE 754 binary16 */
+    ZERO_BF16 = 2      /* bfloat16          */
+};
+
+#define ZERO_MAX_RANKS 16
+
+/* Result of the check phase.  Lives in device memory; written by
+ * zero_unscale_check_norm, read by zero_adamw_step on the device, and copied
+ * to the host by the caller only for the loss-scale update.  16 bytes. */
+typedef struct zero_step_result {
+    double sumsq;        /* sum over the checked elements of (value * inv_scale)^2, fp64 */
+    uint32_t overflow;   /* 1 if some checked element is +-inf or NaN, else 0          */
+    float inv_scale;     /* the unscale factor the check used                           */
+} zero_step_result;
+
+/* AdamW hyper-parameters (wmrh.cn article section 3.1 ds_config: betas,
+ * eps, weight_decay; learning rate per the run).  `step` is t counted from 1,
+ * i.e. the value after this step's increment.  max_grad_norm <= 0 turns
+ * clipping off. */
+typedef struct zero_adamw_hparams {
+    float lr, beta1, beta2, eps, weight_decay, max_grad_norm;
+    int64_t step;
+} zero_adamw_hparams;
+
+/* Dynamic loss-scale state (host).  wmrh.cn article section 3.1 fp16 block:
+ * loss_scale 0 (dynamic), loss_scale_window 1000, min_loss_scale 1. */
+typedef struct zero_loss_scaler {
+    double scale;       /* current loss scale S (a power of two)          */
+    double min_scale;   /* S never drops below this                       */
+    int64_t window;     /* clean steps in a row before S doubles          */
+    int64_t clean;      /* clean steps since the last change              */
+    int64_t skipped;    /* total steps skipped for overflow               */
+} zero_loss_scaler;
+
+/* ---------------------------------------------------------------- host ---- */
+
+/* Flatten + align + partition (ZeRO-2 source walkthrough, section 4.1 steps
+ * 1-2; section 2.1 "near-equal partitions").  Tensors are laid back to back in
+ * the given order: tensor_offsets[k] = numels[0] + ... + numels[k-1].  The
+ * total Phi is padded at the tail to the next multiple of world*align_elems
+ * (the pages use align_elems = 2, i.e. 4 bytes of 16-bit data); partition p
+ * is [part_begin[p], part_begin[p+1]) with part_begin[p] = p * padded/world.
+ *   numels[n_tensors]          host, in     element counts, each >= 0
+ *   tensor_offsets[n_tensors]  host, out    (may be NULL when n_tensors == 0)
+ *   part_begin[world + 1]      host, out
+ *   padded_total               host, out
+ * Errors: ZERO_EINVAL for world < 1, align_elems < 1, a negative count or a
+ * NULL output; ZERO_ERANGE if the padded total overflows int64. */
+int zero_partition_layout(const int64_t* numels, int64_t n_tensors, int32_t world,
+                          int32_t align_elems, int64_t* tensor_offsets, int64_t* part_begin,
+                          int64_t* padded_total);
+
+/* Reduce-bucket windows (ZeRO-2 source walkthrough, section 4.2: gradients are
+ * gathered into buckets of reduce_bucket_size elements and each full bucket
+ * is reduced).  Tensors are taken in order; a bucket that cannot take the
+ * next whole tensor is closed; an empty bucket takes any tensor, however large.
+ *   bucket_first[n_tensors + 1]  host, out  first tensor of each bucket, then n_tensors
+ *   n_buckets                    host, out
+ * Errors: ZERO_EINVAL for bucket_cap < 1, a negative count or a NULL output. */
+int zero_bucket_layout(const int64_t* numels, int64_t n_tensors, int64_t bucket_cap,
+                       int64_t* bucket_first, int64_t* n_buckets);
+
+/* Model-state bytes per rank under ZeRO stage 0..3 (ZeRO 优化器 memory tables;
+ * ZeRO / DeepSpeed 深度解读报告 section 3.3): 2 B of 16-bit parameters, 2 B of
+ * 16-bit gradients and 12 B of fp32 master + m + v per element; stage >= 1
+ * shards the 12 B, stage >= 2 the gradients, stage 3 the parameters.  A
+ * sharded part holds P = padded_total / world elements; unsharded parts hold
+ * numel_total.  With padded_total == numel_total this is 16*Phi,
+ * 4*Phi + 12*Phi/N, 2*Phi + 14*Phi/N and 16*Phi/N.
+ * Errors: ZERO_EINVAL for stage outside 0..3, world < 1, padded_total <
+ * numel_total or not a multiple of world; ZERO_ERANGE on overflow. */
+int zero_memory_bytes(int32_t stage, int64_t numel_total, int64_t padded_total, int32_t world,
+                      int64_t* bytes_out);
+
+/* Dynamic loss-scale update after a step (wmrh.cn article section 3.1).  On
+ * overflow: S = max(S/2, min_scale), clean = 0, skipped += 1.  Otherwise
+ * clean += 1 and, when clean reaches window, S = 2S and clean = 0.
+ * Errors: ZERO_EINVAL for a NULL state or window < 1. */
+int zero_loss_scaler_update(zero_loss_scaler* scaler, uint32_t overflow);
+
+/* Text for a status code (static storage). */
+const char* zero_status_str(int status);
+
+/* -------------------------------------------------------------- device ---- */
+
+/* fp32 master weights of a partition from its 16-bit copy: master[i] =
+ * float(param16[i]), exact (ZeRO-2 source walkthrough, section 4.1 step 3:
+ * each rank clones its 16-bit partition to fp32).
+ *   master[count]   device, out (fp32)
+ *   param16[count]  device, in  (16-bit patterns of `dtype`) */
+int zero_init_master(float* master, const void* param16, int64_t count, int32_t dtype,
+                     hipStream_t stream);
+
+/* Reduce to the owner: dst[i] = round16(g_0[i] + g_1[i] + ... + g_{N-1}[i]),
+ * the additions done in fp64 in rank order and the result rounded once to
+ * the 16-bit type, ties to even (exact for binary16: every fp64 partial sum
+ * of at most 16 binary16 values is exact).  An inf/NaN input or a sum beyond
+ * the 16-bit range gives inf/NaN in dst, which the check phase then flags.
+ * (ZeRO 优化器 "ZeRO Stage 1": after the reduce the owner holds the sum of all
+ * ranks' gradients; ZeRO-2 source walkthrough section 三: the reduced data is
+ * fp16/bf16.)
+ *   dst[count]       device, out
+ *   srcs[n_ranks]    host array of device pointers, each to count 16-bit values
+ *   n_ranks          1 .. ZERO_MAX_RANKS
+ * dst may be the same pointer as one srcs[k] (in-place into the owner's own
+ * buffer); no other overlap is allowed. */
+int zero_reduce_owned(void* dst, const void* const* srcs, int32_t n_ranks, int64_t count,
+                      int32_t dtype, hipStream_t stream);
+
+/* Bytes of device workspace zero_unscale_check_norm needs for `count`
+ * elements (at most 32 KiB). */
+size_t zero_check_workspace_bytes(int64_t count);
+
+/* Unscale + overflow check + squared norm over grad16[0, count):
+ *   overflow = some element is +-inf or NaN (exponent field all ones);
+ *   sumsq    = sum of ((double)value * inv_scale)^2, accumulated in fp64
+ *              (each square is exact; the summation order is fixed for a
+ *              given count, so repeated calls give identical bits).
+ * With accumulate == 0 the call overwrites *res; with accumulate != 0 it adds
+ * its sumsq to res->sumsq and ORs its flag into res->overflow, so several
+ * owner ranges checked in turn on one stream form one global result.
+ * res->inv_scale is set to inv_scale either way.
+ *   grad16[count]   device, in
+ *   inv_scale       1 / (loss scale * divisor), a power of two for an exact unscale
+ *   res             device, out (in/out when accumulating)
+ *   workspace       device scratch of at least zero_check_workspace_bytes(count)
+ *                   bytes; its contents are overwritten, need no initialisation
+ *                   and must not be shared by calls that may overlap. */
+int zero_unscale_check_norm(const void* grad16, int64_t count, int32_t dtype, float inv_scale,
+                            zero_step_result* res, void* workspace, size_t workspace_bytes,
+                            int32_t accumulate, hipStream_t stream);
+
+/* Fused AdamW over one partition (decoupled weight decay with bias-corrected
+ * moments, eps added after the square root), reading the check result on the
+ * device: if res->overflow is set the kernel writes nothing (the step is
+ * skipped; the caller keeps t).  Otherwise, with
+ *   coef = max_grad_norm / (sqrt(res->sumsq) + 1e-6) if max_grad_norm > 0 and
+ *          that ratio is below 1, else 1                     (computed in fp64,
+ *          then rounded to fp32)
+ * and fp32 constants rounded once from fp64: decay = 1 - lr*wd, 1 - beta1,
+ * 1 - beta2, bc1 = 1 - beta1^t, bc2 = 1 - beta2^t, each element does, in fp32
+ * with one rounding per operation and no fused multiply-add:
+ *   g  = (value(grad16[i]) * inv_scale) * coef
+ *   p  = master[i] * decay
+ *   m  = beta1 * m + (1 - beta1) * g
+ *   v  = beta2 * v + (1 - beta2) * (g * g)
+ *   p  = p - lr * ((m / bc1) / (sqrt(v / bc2) + eps))
+ *   master[i] = p; exp_avg[i] = m; exp_avg_sq[i] = v; param16[i] = round16(p)
+ * (round16: nearest, ties to even).
+ *   master, exp_avg, exp_avg_sq [count]  device, in/out, fp32
+ *   param16[count]                        device, out, 16-bit copy
+ *   grad16[count]                         device, in, the reduced gradient
+ *   hp                                    host, read during the call
+ *   res                                   device, in: written by the check phase
+ * Errors: ZERO_EINVAL for NULL pointers, count < 0, hp->step < 1 or an
+ * unknown dtype. */
+int zero_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
+                    const void* grad16, int64_t count, int32_t dtype,
+                    const zero_adamw_hparams* hp, const zero_step_result* res,
+                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

@@ -81,6 +81,7 @@ def _dev_lib():
     if _dev is None:
         if not os.path.exists(DEV_LIB):
             raise RuntimeError(f"{DEV_LIB} is missing: run __graft_entry__.build() first")
+        import torch  # noqa: F401  (bind to the HIP runtime torch loaded)
         lib = ctypes.CDLL(DEV_LIB)
         lib.synth_dev_fill.restype = ctypes.c_int
         lib.synth_dev_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,

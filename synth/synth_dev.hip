@@ -20,7 +20,8 @@ __global__ void __launch_bounds__(256) fill_kernel(uint16_t* __restrict__ out, i
 
 extern "C" {
 
-// Returns 0 on success, -1 on bad arguments, -3 on a launch error.
+// Returns 0 on success, -1 on bad arguments, or the (positive) hipError_t of
+// a failed launch.
 int synth_dev_fill(void* out, int64_t n, uint64_t first, uint64_t key, int64_t mult, int32_t e,
                    int32_t exp_bits, int32_t frac_bits, void* stream) {
     if (n < 0 || (n > 0 && out == nullptr)) return -1;
@@ -28,9 +29,12 @@ int synth_dev_fill(void* out, int64_t n, uint64_t first, uint64_t key, int64_t m
     if (n == 0) return 0;
     int64_t blocks = (n + 255) / 256;
     if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                       (uint16_t*)out, n, first, key, mult, (int)e, (int)exp_bits, (int)frac_bits);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    uint16_t* o = (uint16_t*)out;
+    int ei = e, eb = exp_bits, fb = frac_bits;
+    void* args[] = {&o, &n, &first, &key, &mult, &ei, &eb, &fb};
+    hipError_t err = hipLaunchKernel((const void*)fill_kernel, dim3((unsigned)blocks), dim3(256),
+                                     args, 0, (hipStream_t)stream);
+    return err == hipSuccess ? 0 : (int)err;
 }
 
 }  // extern "C"

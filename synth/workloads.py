@@ -166,10 +166,33 @@ def _make() -> dict:
         inject_every=4, seed=5,
         description="10,000 tensors log-uniform in [64, 2^20] in 5e8-element reduce buckets, "
                     "N=16, fp16 grads x dynamic loss scale, inf/NaN every 4th step")
+    # the same structure at a size the oracle runs in full in seconds
+    w["buckets_small"] = Workload(
+        name="buckets_small", tensors=bucket_tensors(400, 64, 1 << 14, seed=6), world=16,
+        dtype=FP16, grad_sigma=1e-3, steps=40, scale0=2.0 ** 16, dynamic=True, owners="all",
+        bucket_cap=400_000, inject_every=4, seed=6,
+        description="400 tensors log-uniform in [64, 2^14] in 4e5-element reduce buckets, "
+                    "N=16, dynamic loss scale, inf/NaN every 4th step")
+    w["toy_tiny"] = Workload(
+        name="toy_tiny", tensors=toy_tensors(hidden=64, layers=2, classes=10), world=8,
+        dtype=FP16, grad_sigma=1e-3, steps=3, scale0=2.0 ** 16, dynamic=True, seed=9,
+        description="ToyModel with hidden 64 and 2 layers (smoke size)")
     return w
 
 
 WORKLOADS = _make()
+
+
+def bucket_windows(wl: Workload, offsets: np.ndarray, padded: int, bucket_first: np.ndarray):
+    """Element ranges [a, b) of the reduce buckets; the last one takes the
+    alignment padding."""
+    out = []
+    nb = bucket_first.size - 1
+    for k in range(nb):
+        a = int(offsets[bucket_first[k]]) if bucket_first[k] < len(offsets) else wl.phi
+        b = int(offsets[bucket_first[k + 1]]) if k + 1 < nb else padded
+        out.append((a, b))
+    return out
 
 
 def tensor_segments(wl: Workload, offsets: np.ndarray, begin: int, end: int):

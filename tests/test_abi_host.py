@@ -1,0 +1,100 @@
+"""The C-ABI library on the CPU (no GPU calls): it loads, exports every
+function include/zero_shard.h declares, and its host-side logic (layout,
+bucket windows, memory bytes, loss scaler) agrees with the oracle exactly."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import workloads as W
+import zero_partitioned_mixed_shard_amd as Z
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "zero_shard.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    lib = Z.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(Z.EXPORTS)
+
+
+@pytest.mark.parametrize("name", sorted(W.WORKLOADS))
+def test_layout_matches_oracle_on_workloads(name):
+    wl = W.WORKLOADS[name]
+    a = Z.zero_partition_layout(wl.numels, wl.world, wl.align)
+    b = oracle.layout(wl.numels, wl.world, wl.align)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+def test_layout_matches_oracle_random():
+    rng = np.random.default_rng(2)
+    for _ in range(2000):
+        n = int(rng.integers(0, 8))
+        numels = rng.integers(0, 1 << int(rng.integers(1, 30)), n)
+        world = int(rng.integers(1, 17))
+        align = int(rng.choice([1, 2, 4, 8]))
+        a = Z.zero_partition_layout(numels, world, align)
+        b = oracle.layout(numels, world, align)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+def test_layout_errors():
+    for args in (([1, 2], 0, 2), ([1, 2], 2, 0), ([1, -2], 2, 2)):
+        with pytest.raises(Z.ZeroError):
+            Z.zero_partition_layout(*args)
+    with pytest.raises(Z.ZeroError, match="range"):
+        Z.zero_partition_layout([2 ** 62, 2 ** 62, 2 ** 62], 2, 2)
+
+
+def test_buckets_match_oracle():
+    rng = np.random.default_rng(3)
+    for _ in range(2000):
+        n = int(rng.integers(1, 20))
+        numels = rng.integers(0, 50, n)
+        cap = int(rng.integers(1, 80))
+        assert np.array_equal(Z.zero_bucket_layout(numels, cap), oracle.buckets(numels, cap))
+    wl = W.WORKLOADS["buckets"]
+    assert np.array_equal(Z.zero_bucket_layout(wl.numels, wl.bucket_cap),
+                          oracle.buckets(wl.numels, wl.bucket_cap))
+
+
+def test_memory_bytes_match_oracle():
+    for name, wl in W.WORKLOADS.items():
+        _, _, padded = oracle.layout(wl.numels, wl.world, wl.align)
+        for stage in range(4):
+            assert Z.zero_memory_bytes(stage, wl.phi, padded, wl.world) == \
+                oracle.memory_bytes(stage, wl.phi, wl.world, padded)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_memory_bytes(4, 10, 10, 1)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_memory_bytes(1, 10, 9, 1)
+
+
+def test_loss_scaler_matches_oracle():
+    rng = np.random.default_rng(4)
+    for window in (1, 2, 3, 1000):
+        a = Z.zero_loss_scaler(2.0 ** 16, 1.0, window, 0, 0)
+        b = oracle.Scaler(2.0 ** 16, 1.0, window)
+        for f in (rng.random(3000) < 0.3).astype(int):
+            Z.zero_loss_scaler_update(a, int(f))
+            b.update(int(f))
+            assert (a.scale, a.clean, a.skipped) == (b.scale, b.clean, b.skipped)
+
+
+def test_status_strings():
+    assert Z.zero_status_str(Z.ZERO_OK) == "ok"
+    assert "invalid" in Z.zero_status_str(Z.ZERO_EINVAL)
+    assert Z.zero_check_workspace_bytes(0) > 0
+    assert Z.zero_check_workspace_bytes(10 ** 12) <= 32 * 1024

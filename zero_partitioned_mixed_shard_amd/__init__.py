@@ -1,0 +1,232 @@
+"""Python binding of the ZeRO-1/2 owner-shard step library (libzero_shard.so).
+
+Argument marshalling only: every phase runs in the HIP kernels of
+``csrc/zero_shard.hip`` behind the C ABI of ``include/zero_shard.h``.  The
+functions keep the C names.  Device buffers are torch tensors (device memory
+and streams are all torch is used for); 16-bit data is passed as
+torch.float16 / torch.bfloat16 tensors, fp32 state as torch.float32.  There is no fallback: if the library is missing, importing
+this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libzero_shard.so")
+
+ZERO_OK, ZERO_EINVAL, ZERO_ERANGE, ZERO_EDEVICE = 0, -1, -2, -3
+ZERO_FP16, ZERO_BF16 = 1, 2
+ZERO_MAX_RANKS = 16
+
+
+class zero_step_result(ctypes.Structure):
+    _fields_ = [("sumsq", ctypes.c_double), ("overflow", ctypes.c_uint32),
+                ("inv_scale", ctypes.c_float)]
+
+
+class zero_adamw_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("max_grad_norm", ctypes.c_float), ("step", ctypes.c_int64)]
+
+
+class zero_loss_scaler(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_double), ("min_scale", ctypes.c_double),
+                ("window", ctypes.c_int64), ("clean", ctypes.c_int64),
+                ("skipped", ctypes.c_int64)]
+
+
+RESULT_BYTES = ctypes.sizeof(zero_step_result)   # 16
+
+EXPORTS = (
+    "zero_partition_layout", "zero_bucket_layout", "zero_memory_bytes",
+    "zero_loss_scaler_update", "zero_status_str", "zero_init_master", "zero_reduce_owned",
+    "zero_check_workspace_bytes", "zero_unscale_check_norm", "zero_adamw_step",
+)
+
+
+class ZeroError(RuntimeError):
+    pass
+
+
+def _hip_runtimes() -> set:
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return set()
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    # torch brings its own HIP runtime; load it first so that this library
+    # binds to the same one (two runtimes in one process do not share devices)
+    import torch  # noqa: F401
+    L = ctypes.CDLL(LIB_PATH)
+    if len(_hip_runtimes()) > 1:
+        raise ImportError(f"more than one HIP runtime is loaded: {sorted(_hip_runtimes())}")
+    P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    sig = {
+        "zero_partition_layout": ([P, i64, i32, i32, P, P, P], ctypes.c_int),
+        "zero_bucket_layout": ([P, i64, i64, P, P], ctypes.c_int),
+        "zero_memory_bytes": ([i32, i64, i64, i32, P], ctypes.c_int),
+        "zero_loss_scaler_update": ([P, ctypes.c_uint32], ctypes.c_int),
+        "zero_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        "zero_init_master": ([P, P, i64, i32, P], ctypes.c_int),
+        "zero_reduce_owned": ([P, P, i32, i64, i32, P], ctypes.c_int),
+        "zero_check_workspace_bytes": ([i64], ctypes.c_size_t),
+        "zero_unscale_check_norm": ([P, i64, i32, f32, P, P, ctypes.c_size_t, i32, P],
+                                    ctypes.c_int),
+        "zero_adamw_step": ([P, P, P, P, P, i64, i32, P, P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != ZERO_OK:
+        raise ZeroError(f"{what}: {_lib.zero_status_str(rc).decode()} ({rc})")
+
+
+# ------------------------------------------------------------ marshalling --
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return ZERO_FP16
+    if t.dtype == torch.bfloat16:
+        return ZERO_BF16
+    raise TypeError(f"16-bit tensor expected, got {t.dtype}")
+
+
+def _dev(t, nbytes_per: int, count: int, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.element_size() != nbytes_per or t.numel() < count:
+        raise ValueError(f"{name}: need {count} elements of {nbytes_per} bytes")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ host ---
+def zero_partition_layout(numels: Sequence[int], world: int, align_elems: int = 2):
+    """-> (tensor_offsets int64[n], part_begin int64[world+1], padded_total)."""
+    n = np.ascontiguousarray(numels, dtype=np.int64)
+    offs = np.zeros(max(1, n.size), dtype=np.int64)
+    parts = np.zeros(max(1, world + 1), dtype=np.int64)
+    padded = ctypes.c_int64(0)
+    _check(_lib.zero_partition_layout(n.ctypes.data, n.size, world, align_elems, offs.ctypes.data,
+                                      parts.ctypes.data, ctypes.byref(padded)),
+           "zero_partition_layout")
+    return offs[:n.size].copy(), parts, padded.value
+
+
+def zero_bucket_layout(numels: Sequence[int], bucket_cap: int) -> np.ndarray:
+    """-> bucket_first int64[n_buckets + 1]."""
+    n = np.ascontiguousarray(numels, dtype=np.int64)
+    first = np.zeros(n.size + 1, dtype=np.int64)
+    nb = ctypes.c_int64(0)
+    _check(_lib.zero_bucket_layout(n.ctypes.data, n.size, bucket_cap, first.ctypes.data,
+                                   ctypes.byref(nb)), "zero_bucket_layout")
+    return first[:nb.value + 1].copy()
+
+
+def zero_memory_bytes(stage: int, numel_total: int, padded_total: int, world: int) -> int:
+    out = ctypes.c_int64(0)
+    _check(_lib.zero_memory_bytes(stage, numel_total, padded_total, world, ctypes.byref(out)),
+           "zero_memory_bytes")
+    return out.value
+
+
+def zero_loss_scaler_update(scaler: zero_loss_scaler, overflow: int) -> zero_loss_scaler:
+    _check(_lib.zero_loss_scaler_update(ctypes.byref(scaler), int(bool(overflow))),
+           "zero_loss_scaler_update")
+    return scaler
+
+
+def zero_status_str(status: int) -> str:
+    return _lib.zero_status_str(status).decode()
+
+
+def zero_check_workspace_bytes(count: int) -> int:
+    return int(_lib.zero_check_workspace_bytes(count))
+
+
+# ---------------------------------------------------------------- device ---
+def zero_init_master(master, param16, count: Optional[int] = None, stream=None) -> None:
+    count = param16.numel() if count is None else count
+    _check(_lib.zero_init_master(_dev(master, 4, count, "master"), _dev(param16, 2, count, "param16"),
+                                 count, _dtype_code(param16), _stream(stream)), "zero_init_master")
+
+
+def zero_reduce_owned(dst, srcs: Sequence, count: Optional[int] = None, stream=None) -> None:
+    count = dst.numel() if count is None else count
+    dt = _dtype_code(dst)
+    if not 1 <= len(srcs) <= ZERO_MAX_RANKS:
+        raise ValueError("1..16 rank buffers")
+    for s in srcs:
+        if _dtype_code(s) != dt:
+            raise TypeError("rank buffers and dst must share the 16-bit type")
+    ptrs = (ctypes.c_void_p * len(srcs))(*[_dev(s, 2, count, "src") for s in srcs])
+    _check(_lib.zero_reduce_owned(_dev(dst, 2, count, "dst"), ptrs, len(srcs), count, dt,
+                                  _stream(stream)), "zero_reduce_owned")
+
+
+def zero_unscale_check_norm(grad16, inv_scale: float, res, workspace, accumulate: bool = False,
+                            count: Optional[int] = None, stream=None) -> None:
+    """res: a device tensor of >= 16 bytes holding one zero_step_result."""
+    count = grad16.numel() if count is None else count
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    _check(_lib.zero_unscale_check_norm(_dev(grad16, 2, count, "grad16"), count,
+                                        _dtype_code(grad16), float(inv_scale), res.data_ptr(),
+                                        _dev(workspace, workspace.element_size(), 0, "workspace"),
+                                        ws_bytes, int(bool(accumulate)), _stream(stream)),
+           "zero_unscale_check_norm")
+
+
+def zero_adamw_step(master, exp_avg, exp_avg_sq, param16, grad16, hp: zero_adamw_hparams, res,
+                    count: Optional[int] = None, stream=None) -> None:
+    count = master.numel() if count is None else count
+    dt = _dtype_code(grad16)
+    if _dtype_code(param16) != dt:
+        raise TypeError("param16 and grad16 must share the 16-bit type")
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    _check(_lib.zero_adamw_step(_dev(master, 4, count, "master"), _dev(exp_avg, 4, count, "exp_avg"),
+                                _dev(exp_avg_sq, 4, count, "exp_avg_sq"),
+                                _dev(param16, 2, count, "param16"), _dev(grad16, 2, count, "grad16"),
+                                count, dt, ctypes.byref(hp), res.data_ptr(), _stream(stream)),
+           "zero_adamw_step")
+
+
+def read_result(res) -> zero_step_result:
+    """Copy a device zero_step_result to the host (synchronises the stream)."""
+    raw = res.detach().cpu().numpy().tobytes()[:RESULT_BYTES]
+    return zero_step_result.from_buffer_copy(raw)

@@ -1,0 +1,132 @@
+"""Owner-shard step driver: device buffers plus the ABI calls in order.
+
+Holds the fp32 master / m / v, the 16-bit parameter copy, the reduced
+gradient, the 16-byte step result and the check workspace for one simulated
+region of the flat buffer (one owner's partition, or several owners'), and
+runs one step as the library's calls:
+
+  for each reduce window (bucket x owner)   zero_reduce_owned
+  for each owner                            zero_unscale_check_norm (owners after
+                                            the first accumulate: one global
+                                            flag and norm)
+  for each owner                            zero_adamw_step (skips on overflow,
+                                            on the device)
+  16-byte readback                          zero_loss_scaler_update, t
+
+Nothing here computes on the data; it sequences calls and keeps host scalars.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import (RESULT_BYTES, ZERO_BF16, ZERO_FP16, read_result, zero_adamw_hparams,
+               zero_adamw_step, zero_check_workspace_bytes, zero_init_master,
+               zero_loss_scaler, zero_loss_scaler_update, zero_reduce_owned,
+               zero_unscale_check_norm)
+
+
+@dataclass
+class StepInfo:
+    overflow: int
+    sumsq: float
+    applied: bool
+    scale_used: float
+    t: int
+
+
+class ShardStep:
+    """State and step of the owners whose partitions lie in [begin, end)."""
+
+    def __init__(self, begin: int, end: int, owners: Sequence[Tuple[int, int]], dtype: int,
+                 lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.0,
+                 scale0=1.0, min_scale=1.0, window=1000, windows: Optional[Sequence[Tuple[int, int]]] = None,
+                 divisor: int = 1, in_place_rank: Optional[int] = None, device="cuda"):
+        self.begin, self.end = begin, end
+        self.count = end - begin
+        self.owners = [(a - begin, b - begin) for a, b in owners]
+        for a, b in self.owners:
+            assert 0 <= a <= b <= self.count
+        self.dtype = dtype
+        self.tdtype = torch.float16 if dtype == ZERO_FP16 else torch.bfloat16
+        self.hp = zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, max_grad_norm, 0)
+        self.scaler = zero_loss_scaler(scale0, min_scale, window, 0, 0)
+        self.divisor = divisor
+        self.t = 0
+        self.in_place_rank = in_place_rank
+        # reduce windows = buckets intersected with owner partitions
+        bounds = [(begin, end)] if windows is None else windows
+        self.reduce_ranges = []
+        for a, b in self.owners:
+            for wa, wb in bounds:
+                lo, hi = max(a, wa - begin), min(b, wb - begin)
+                if lo < hi:
+                    self.reduce_ranges.append((lo, hi))
+        n = self.count
+        self.master = torch.empty(n, dtype=torch.float32, device=device)
+        self.exp_avg = torch.zeros(n, dtype=torch.float32, device=device)
+        self.exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=device)
+        self.param16 = torch.empty(n, dtype=self.tdtype, device=device)
+        self.red = None if in_place_rank is not None else torch.empty(n, dtype=self.tdtype,
+                                                                      device=device)
+        self.res = torch.zeros(RESULT_BYTES // 4, dtype=torch.int32, device=device)
+        ws = max(zero_check_workspace_bytes(b - a) for a, b in self.owners) if self.owners else 8
+        self.workspace = torch.empty((ws + 7) // 8, dtype=torch.float64, device=device)
+
+    # ---------------------------------------------------------------- state
+    def load_param16(self, param16: torch.Tensor) -> None:
+        self.param16.copy_(param16)
+        zero_init_master(self.master, self.param16)
+        self.exp_avg.zero_()
+        self.exp_avg_sq.zero_()
+
+    @property
+    def scale(self) -> float:
+        return self.scaler.scale
+
+    @property
+    def inv_scale(self) -> float:
+        return 1.0 / (self.scaler.scale * self.divisor)
+
+    # ----------------------------------------------------------------- step
+    def reduced(self, rank_bufs: Sequence[torch.Tensor]) -> torch.Tensor:
+        return rank_bufs[self.in_place_rank] if self.red is None else self.red
+
+    def launch(self, rank_bufs: Sequence[torch.Tensor], marks: Optional[List] = None) -> None:
+        """Enqueue reduce -> check -> AdamW on the current stream.  `marks`
+        (4 events) are recorded before reduce, check, AdamW and after."""
+        red = self.reduced(rank_bufs)
+        if marks:
+            marks[0].record()
+        for a, b in self.reduce_ranges:
+            zero_reduce_owned(red[a:b], [r[a:b] for r in rank_bufs])
+        if marks:
+            marks[1].record()
+        inv = self.inv_scale
+        for k, (a, b) in enumerate(self.owners):
+            zero_unscale_check_norm(red[a:b], inv, self.res, self.workspace, accumulate=k > 0)
+        if marks:
+            marks[2].record()
+        self.hp.step = self.t + 1
+        for a, b in self.owners:
+            zero_adamw_step(self.master[a:b], self.exp_avg[a:b], self.exp_avg_sq[a:b],
+                            self.param16[a:b], red[a:b], self.hp, self.res)
+        if marks:
+            marks[3].record()
+
+    def finish(self) -> StepInfo:
+        """Read the 16-byte result (synchronises) and update t and the scaler."""
+        r = read_result(self.res)
+        used = self.scaler.scale
+        applied = not r.overflow
+        if applied:
+            self.t += 1
+        zero_loss_scaler_update(self.scaler, r.overflow)
+        return StepInfo(int(r.overflow), float(r.sumsq), applied, used, self.t)
+
+    def step(self, rank_bufs: Sequence[torch.Tensor], marks: Optional[List] = None) -> StepInfo:
+        self.launch(rank_bufs, marks)
+        return self.finish()
