@@ -2,9 +2,11 @@
 
 One step = the whole owner-shard path over one batch of synthetic gradients
 already resident in HBM:
-  layout (host) -> reduce N ranks' 16-bit gradients to the owner (HIP)
-  -> unscale + overflow check + squared norm (HIP) -> fused AdamW + 16-bit copy
+  layout (host) -> reduce N ranks' 16-bit gradients to the owner fused with
+  unscale + overflow check + squared norm (HIP) -> fused AdamW + 16-bit copy
   (HIP) -> 16-byte result readback -> loss-scale update (host)
+Algorithmic HBM bytes per owned element: 2N + 2 for reduce+check (2N + 4 with
+--unfused, which re-reads the reduced gradient), 28 for AdamW.
 
 Default workload: owner 0's partition of the LLaMA-7B-shaped flat buffer
 (6,738,415,616 parameters, N = 8 ranks, 842,301,952 owned elements, bf16
@@ -44,6 +46,8 @@ def parse():
                     help="wall-clock budget of the CPU oracle leg")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (for HBM counter scaling)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate reduce and check calls instead of the fused one")
     return ap.parse_args()
 
 
@@ -126,7 +130,8 @@ def main():
     shard = ShardStep(begin, end, [(begin, end)], wl.dtype, lr=wl.lr, beta1=wl.beta1,
                       beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
-                      window=wl.window, in_place_rank=0 if in_place else None)
+                      window=wl.window, in_place_rank=0 if in_place else None,
+                      fused=not args.unfused)
     shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16.clone()))
     bufs = [I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded) for r in range(wl.world)]
     torch.cuda.synchronize()
@@ -163,12 +168,19 @@ def main():
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
 
-    ms = {"reduce": [], "check": [], "adamw": []}
-    for e in ev:
-        ms["reduce"].append(e[0].elapsed_time(e[1]))
-        ms["check"].append(e[1].elapsed_time(e[2]))
-        ms["adamw"].append(e[2].elapsed_time(e[3]))
-    bytes_per = {"reduce": 2 * wl.world + 2, "check": 2, "adamw": 28}
+    if args.unfused:
+        ms = {"reduce": [], "check": [], "adamw": []}
+        for e in ev:
+            ms["reduce"].append(e[0].elapsed_time(e[1]))
+            ms["check"].append(e[1].elapsed_time(e[2]))
+            ms["adamw"].append(e[2].elapsed_time(e[3]))
+        bytes_per = {"reduce": 2 * wl.world + 2, "check": 2, "adamw": 28}
+    else:
+        ms = {"reduce_check": [], "adamw": []}
+        for e in ev:
+            ms["reduce_check"].append(e[0].elapsed_time(e[2]))
+            ms["adamw"].append(e[2].elapsed_time(e[3]))
+        bytes_per = {"reduce_check": 2 * wl.world + 2, "adamw": 28}
     phases = {}
     for k, v in ms.items():
         avg = float(np.mean(v))
@@ -200,6 +212,7 @@ def main():
             "grad_dtype": "bf16" if wl.dtype == Z.ZERO_BF16 else "fp16",
             "clip": wl.clip,
             "in_place_reduce": in_place,
+            "fused_reduce_check": not args.unfused,
             "parallelism": "one owner partition on one GPU (N ranks simulated in HBM)",
         },
         "step_GBps": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),

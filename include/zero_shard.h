@@ -165,25 +165,41 @@ int zero_init_master(float* master, const void* param16, int64_t count, int32_t 
 int zero_reduce_owned(void* dst, const void* const* srcs, int32_t n_ranks, int64_t count,
                       int32_t dtype, hipStream_t stream);
 
-/* Bytes of device workspace zero_unscale_check_norm needs for `count`
- * elements (at most 32 KiB). */
+/* Reduce to the owner and check, fused: the same result as
+ * zero_reduce_owned(dst, srcs, ...) followed by zero_unscale_check_norm(dst,
+ * ...), in one pass that never re-reads dst (2 bytes per element less HBM
+ * traffic).  Arguments as in those two calls.  Reduce windows of one step
+ * (bucket x owner ranges) checked in turn on one stream form one global
+ * result when every call after the first passes accumulate != 0. */
+int zero_reduce_check_owned(void* dst, const void* const* srcs, int32_t n_ranks, int64_t count,
+                            int32_t dtype, float inv_scale, zero_step_result* res,
+                            void* workspace, size_t workspace_bytes, int32_t accumulate,
+                            hipStream_t stream);
+
+/* Bytes of device workspace that zero_unscale_check_norm and
+ * zero_reduce_check_owned need for `count` elements: one 12-byte partial per
+ * 2048 elements plus the fold levels (about count / 170 bytes; 50.6 MB for
+ * 8.6e9 elements, 64 bytes minimum). */
 size_t zero_check_workspace_bytes(int64_t count);
 
 /* Unscale + overflow check + squared norm over grad16[0, count):
  *   overflow = some element is +-inf or NaN (exponent field all ones);
  *   sumsq    = sum of ((double)value * inv_scale)^2, accumulated in fp64
  *              (each square is exact; the summation order is fixed for a
- *              given count, so repeated calls give identical bits).
+ *              given count and pointer alignment, so repeated calls give
+ *              identical bits).
  * With accumulate == 0 the call overwrites *res; with accumulate != 0 it adds
  * its sumsq to res->sumsq and ORs its flag into res->overflow, so several
  * owner ranges checked in turn on one stream form one global result.
  * res->inv_scale is set to inv_scale either way.
  *   grad16[count]   device, in
- *   inv_scale       1 / (loss scale * divisor), a power of two for an exact unscale
+ *   inv_scale       1 / (loss scale * divisor), finite and > 0 (ZERO_EINVAL
+ *                   otherwise); a power of two makes the unscale exact
  *   res             device, out (in/out when accumulating)
  *   workspace       device scratch of at least zero_check_workspace_bytes(count)
- *                   bytes; its contents are overwritten, need no initialisation
- *                   and must not be shared by calls that may overlap. */
+ *                   bytes, 8-byte aligned; its contents are overwritten, need
+ *                   no initialisation and must not be shared by calls that may
+ *                   overlap. */
 int zero_unscale_check_norm(const void* grad16, int64_t count, int32_t dtype, float inv_scale,
                             zero_step_result* res, void* workspace, size_t workspace_bytes,
                             int32_t accumulate, hipStream_t stream);

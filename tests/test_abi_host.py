@@ -96,5 +96,9 @@ def test_loss_scaler_matches_oracle():
 def test_status_strings():
     assert Z.zero_status_str(Z.ZERO_OK) == "ok"
     assert "invalid" in Z.zero_status_str(Z.ZERO_EINVAL)
-    assert Z.zero_check_workspace_bytes(0) > 0
-    assert Z.zero_check_workspace_bytes(10 ** 12) <= 32 * 1024
+    assert Z.zero_check_workspace_bytes(0) >= 16
+    # one 12-byte partial per 2048 elements plus the fold levels
+    for n in (1, 2047, 2048, 10 ** 6, 842_301_952, 8_622_081_024, 10 ** 12):
+        ws = Z.zero_check_workspace_bytes(n)
+        assert 12 * (n // 2048) <= ws <= n / 170 + 1024
+    assert Z.zero_check_workspace_bytes(8_622_081_024) < 51e6

@@ -144,7 +144,7 @@ def _ws(count):
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])
-@pytest.mark.parametrize("count", COUNTS + [3_000_017])
+@pytest.mark.parametrize("count", COUNTS + [3_000_017, 10_000_019])
 @pytest.mark.parametrize("offset", [0, 5])
 @pytest.mark.parametrize("specials", [0.0, 1e-4])
 def test_check_parity(dtype, count, offset, specials):
@@ -161,6 +161,61 @@ def test_check_parity(dtype, count, offset, specials):
     assert r.inv_scale == inv
     if not flag:
         assert r.sumsq == pytest.approx(sumsq, rel=1e-12, abs=0)
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("n_ranks", [1, 3, 8, 16])
+@pytest.mark.parametrize("count", COUNTS + [10_000_019])
+@pytest.mark.parametrize("offset", [0, 3])
+def test_reduce_check_fused_parity(dtype, n_ranks, count, offset):
+    """zero_reduce_check_owned = reduce then check; 10,000,019 elements need
+    two fold levels of block partials."""
+    if count > 1_000_000 and n_ranks not in (8, 16):
+        pytest.skip("large size only at the workload rank counts")
+    rng = np.random.default_rng(7 * dtype + 31 * n_ranks + count % 101 + offset)
+    host = [_rand16(count, dtype, rng, specials=0.0 if count > 1000 else 0.01)
+            for _ in range(n_ranks)]
+    srcs = [_dev16(h, dtype, offset) for h in host]
+    dst = _dev16(np.zeros(count, np.uint16), dtype, offset)
+    inv = 2.0 ** -10
+    res = _res_tensor()
+    Z.zero_reduce_check_owned(dst, srcs, inv, res, _ws(count))
+    r = Z.read_result(res)
+    want = oracle.reduce(host, dtype) if count else np.zeros(0, np.uint16)
+    if count:
+        assert_bits16_equal(to_np16(dst), want, dtype, "fused reduce")
+    flag, sumsq = oracle.check(want, dtype, inv)
+    assert r.overflow == flag and r.inv_scale == inv
+    if not flag:
+        assert r.sumsq == pytest.approx(sumsq, rel=1e-12, abs=0)
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_reduce_check_fused_unaligned_and_windows(dtype):
+    rng = np.random.default_rng(17)
+    count = 3_000_001
+    host = [_rand16(count, dtype, rng) for _ in range(8)]
+    want = oracle.reduce(host, dtype)
+    # sources at different alignments: every lane walks its 8 elements one by one
+    srcs = [_dev16(h, dtype, k % 3) for k, h in enumerate(host)]
+    dst = _dev16(np.zeros(count, np.uint16), dtype, 1)
+    res = _res_tensor()
+    Z.zero_reduce_check_owned(dst, srcs, 1.0, res, _ws(count))
+    r = Z.read_result(res)
+    assert_bits16_equal(to_np16(dst), want, dtype, "fused, mixed alignment")
+    flag, sumsq = oracle.check(want, dtype, 1.0)
+    assert r.overflow == flag == 0 and r.sumsq == pytest.approx(sumsq, rel=1e-12)
+    # three windows accumulated into one result, a NaN in the middle one
+    srcs = [_dev16(h, dtype) for h in host]
+    srcs[4][1_500_000] = float("nan")
+    dst = _dev16(np.zeros(count, np.uint16), dtype)
+    cuts = [0, 1_000_000, 2_000_003, count]
+    ws = _ws(count)
+    for k in range(3):
+        a, b = cuts[k], cuts[k + 1]
+        Z.zero_reduce_check_owned(dst[a:b], [x[a:b] for x in srcs], 1.0, res, ws,
+                                  accumulate=k > 0)
+    assert Z.read_result(res).overflow == 1
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])

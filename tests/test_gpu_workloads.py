@@ -39,13 +39,14 @@ def _setup(wl, owner_ids):
     return offs, padded, owners, begin, end, windows
 
 
-def run_parity(name, owner_ids, steps=None, threads=4):
+def run_parity(name, owner_ids, steps=None, threads=4, fused=True):
     wl = W.WORKLOADS[name]
     steps = wl.steps if steps is None else steps
     offs, padded, owners, begin, end, windows = _setup(wl, owner_ids)
     shard = ShardStep(begin, end, owners, wl.dtype, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
                       eps=wl.eps, weight_decay=wl.weight_decay, max_grad_norm=wl.clip,
-                      scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window, windows=windows)
+                      scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window, windows=windows,
+                      fused=fused)
     # initial state: device generator on the GPU, host generator for the oracle
     d_p16 = I.device_param16(wl, offs, begin, end)
     h_p16 = I.host_param16(wl, offs, begin, end, threads)
@@ -101,7 +102,10 @@ def test_bert_owner0_all_steps_clip():
     run_parity("bert", [0])
 
 
-def test_buckets_small_all_owners_dynamic_scaling():
-    shard, scaler, skipped, t = run_parity("buckets_small", list(range(16)))
+@pytest.mark.parametrize("fused", [True, False])
+def test_buckets_small_all_owners_dynamic_scaling(fused):
+    """Fused: one reduce+check call per bucket-x-owner window.  Unfused:
+    reduce per window, then check per owner."""
+    shard, scaler, skipped, t = run_parity("buckets_small", list(range(16)), fused=fused)
     # ten inf/NaN injections in 40 steps: ten halvings of 2^16, t = 30
     assert skipped == 10 and t == 30 and scaler.scale == 64.0

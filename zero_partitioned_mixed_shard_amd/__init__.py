@@ -45,7 +45,8 @@ RESULT_BYTES = ctypes.sizeof(zero_step_result)   # 16
 EXPORTS = (
     "zero_partition_layout", "zero_bucket_layout", "zero_memory_bytes",
     "zero_loss_scaler_update", "zero_status_str", "zero_init_master", "zero_reduce_owned",
-    "zero_check_workspace_bytes", "zero_unscale_check_norm", "zero_adamw_step",
+    "zero_check_workspace_bytes", "zero_unscale_check_norm", "zero_reduce_check_owned",
+    "zero_adamw_step",
 )
 
 
@@ -82,6 +83,8 @@ def _load():
         "zero_reduce_owned": ([P, P, i32, i64, i32, P], ctypes.c_int),
         "zero_check_workspace_bytes": ([i64], ctypes.c_size_t),
         "zero_unscale_check_norm": ([P, i64, i32, f32, P, P, ctypes.c_size_t, i32, P],
+                                    ctypes.c_int),
+        "zero_reduce_check_owned": ([P, P, i32, i64, i32, f32, P, P, ctypes.c_size_t, i32, P],
                                     ctypes.c_int),
         "zero_adamw_step": ([P, P, P, P, P, i64, i32, P, P, P], ctypes.c_int),
     }
@@ -209,6 +212,27 @@ def zero_unscale_check_norm(grad16, inv_scale: float, res, workspace, accumulate
                                         _dev(workspace, workspace.element_size(), 0, "workspace"),
                                         ws_bytes, int(bool(accumulate)), _stream(stream)),
            "zero_unscale_check_norm")
+
+
+def zero_reduce_check_owned(dst, srcs: Sequence, inv_scale: float, res, workspace,
+                            accumulate: bool = False, count: Optional[int] = None,
+                            stream=None) -> None:
+    count = dst.numel() if count is None else count
+    dt = _dtype_code(dst)
+    if not 1 <= len(srcs) <= ZERO_MAX_RANKS:
+        raise ValueError("1..16 rank buffers")
+    for s in srcs:
+        if _dtype_code(s) != dt:
+            raise TypeError("rank buffers and dst must share the 16-bit type")
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    ptrs = (ctypes.c_void_p * len(srcs))(*[_dev(s, 2, count, "src") for s in srcs])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.zero_reduce_check_owned(_dev(dst, 2, count, "dst"), ptrs, len(srcs), count, dt,
+                                        float(inv_scale), res.data_ptr(),
+                                        _dev(workspace, workspace.element_size(), 0, "workspace"),
+                                        ws_bytes, int(bool(accumulate)), _stream(stream)),
+           "zero_reduce_check_owned")
 
 
 def zero_adamw_step(master, exp_avg, exp_avg_sq, param16, grad16, hp: zero_adamw_hparams, res,

@@ -5,13 +5,15 @@ gradient, the 16-byte step result and the check workspace for one simulated
 region of the flat buffer (one owner's partition, or several owners'), and
 runs one step as the library's calls:
 
-  for each reduce window (bucket x owner)   zero_reduce_owned
-  for each owner                            zero_unscale_check_norm (owners after
+  for each reduce window (bucket x owner)   zero_reduce_check_owned (windows after
                                             the first accumulate: one global
                                             flag and norm)
   for each owner                            zero_adamw_step (skips on overflow,
                                             on the device)
   16-byte readback                          zero_loss_scaler_update, t
+
+With fused=False the reduce and the check are separate calls
+(zero_reduce_owned per window, then zero_unscale_check_norm per owner).
 
 Nothing here computes on the data; it sequences calls and keeps host scalars.
 """
@@ -25,8 +27,8 @@ import torch
 
 from . import (RESULT_BYTES, ZERO_BF16, ZERO_FP16, read_result, zero_adamw_hparams,
                zero_adamw_step, zero_check_workspace_bytes, zero_init_master,
-               zero_loss_scaler, zero_loss_scaler_update, zero_reduce_owned,
-               zero_unscale_check_norm)
+               zero_loss_scaler, zero_loss_scaler_update, zero_reduce_check_owned,
+               zero_reduce_owned, zero_unscale_check_norm)
 
 
 @dataclass
@@ -44,7 +46,8 @@ class ShardStep:
     def __init__(self, begin: int, end: int, owners: Sequence[Tuple[int, int]], dtype: int,
                  lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.0,
                  scale0=1.0, min_scale=1.0, window=1000, windows: Optional[Sequence[Tuple[int, int]]] = None,
-                 divisor: int = 1, in_place_rank: Optional[int] = None, device="cuda"):
+                 divisor: int = 1, in_place_rank: Optional[int] = None, fused: bool = True,
+                 device="cuda"):
         self.begin, self.end = begin, end
         self.count = end - begin
         self.owners = [(a - begin, b - begin) for a, b in owners]
@@ -57,6 +60,7 @@ class ShardStep:
         self.divisor = divisor
         self.t = 0
         self.in_place_rank = in_place_rank
+        self.fused = fused
         # reduce windows = buckets intersected with owner partitions
         bounds = [(begin, end)] if windows is None else windows
         self.reduce_ranges = []
@@ -73,7 +77,8 @@ class ShardStep:
         self.red = None if in_place_rank is not None else torch.empty(n, dtype=self.tdtype,
                                                                       device=device)
         self.res = torch.zeros(RESULT_BYTES // 4, dtype=torch.int32, device=device)
-        ws = max(zero_check_workspace_bytes(b - a) for a, b in self.owners) if self.owners else 8
+        spans = [b - a for a, b in self.owners] + [b - a for a, b in self.reduce_ranges]
+        ws = max(zero_check_workspace_bytes(n) for n in spans) if spans else 64
         self.workspace = torch.empty((ws + 7) // 8, dtype=torch.float64, device=device)
 
     # ---------------------------------------------------------------- state
@@ -99,15 +104,22 @@ class ShardStep:
         """Enqueue reduce -> check -> AdamW on the current stream.  `marks`
         (4 events) are recorded before reduce, check, AdamW and after."""
         red = self.reduced(rank_bufs)
+        inv = self.inv_scale
         if marks:
             marks[0].record()
-        for a, b in self.reduce_ranges:
-            zero_reduce_owned(red[a:b], [r[a:b] for r in rank_bufs])
-        if marks:
-            marks[1].record()
-        inv = self.inv_scale
-        for k, (a, b) in enumerate(self.owners):
-            zero_unscale_check_norm(red[a:b], inv, self.res, self.workspace, accumulate=k > 0)
+        if self.fused:
+            for k, (a, b) in enumerate(self.reduce_ranges):
+                zero_reduce_check_owned(red[a:b], [r[a:b] for r in rank_bufs], inv, self.res,
+                                        self.workspace, accumulate=k > 0)
+            if marks:
+                marks[1].record()
+        else:
+            for a, b in self.reduce_ranges:
+                zero_reduce_owned(red[a:b], [r[a:b] for r in rank_bufs])
+            if marks:
+                marks[1].record()
+            for k, (a, b) in enumerate(self.owners):
+                zero_unscale_check_norm(red[a:b], inv, self.res, self.workspace, accumulate=k > 0)
         if marks:
             marks[2].record()
         self.hp.step = self.t + 1
