@@ -150,7 +150,7 @@ def main():
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
                       window=wl.window, in_place_rank=0 if in_place else None,
                       fused=not args.unfused)
-    shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16.clone()))
+    shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16))
     bufs = [I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded) for r in range(wl.world)]
     torch.cuda.synchronize()
 

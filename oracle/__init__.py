@@ -178,12 +178,14 @@ def memory_bytes(stage: int, phi: int, world: int, padded: int | None = None) ->
 # --------------------------------------------------------------------------
 # The step phases
 # --------------------------------------------------------------------------
-def reduce(srcs: Sequence[np.ndarray], dtype: int) -> np.ndarray:
+def reduce(srcs: Sequence[np.ndarray], dtype: int, out: np.ndarray | None = None) -> np.ndarray:
     srcs = [np.ascontiguousarray(s, dtype=np.uint16) for s in srcs]
     n = srcs[0].size
     assert all(s.size == n for s in srcs)
     ptrs = (ctypes.c_void_p * len(srcs))(*[_p(s) for s in srcs])
-    out = np.empty(n, dtype=np.uint16)
+    if out is None:
+        out = np.empty(n, dtype=np.uint16)
+    assert out.dtype == np.uint16 and out.size == n and out.flags.c_contiguous
     lib().oracle_reduce(_p(out), ptrs, len(srcs), n, dtype)
     return out
 

@@ -30,17 +30,23 @@ def host_param16(wl: Workload, offsets: np.ndarray, begin: int, end: int,
 
 
 def host_rank_grads(wl: Workload, step: int, scale: float, begin: int, end: int,
-                    padded: int, threads: int = 1, ranks=None) -> list:
-    """The N ranks' gradients over [begin, end) of the flat buffer."""
+                    padded: int, threads: int = 1, ranks=None, out_bufs=None) -> list:
+    """The N ranks' gradients over [begin, end) of the flat buffer
+    (written into `out_bufs` when given, one uint16 array per rank)."""
     spec = wl.grad_spec(scale)
     phi = wl.phi
     inj = injections(wl, padded).get(step)
     out = []
-    for r in (range(wl.world) if ranks is None else ranks):
-        g = np.zeros(end - begin, dtype=np.uint16)
+    for k, r in enumerate(range(wl.world) if ranks is None else ranks):
+        if out_bufs is None:
+            g = np.zeros(end - begin, dtype=np.uint16)
+        else:
+            g = out_bufs[k][:end - begin]
         stop = min(end, phi)
         if stop > begin:
             fill_host(g[:stop - begin], begin, wl.grad_key(step, r), spec, threads)
+        if end > max(stop, begin):
+            g[max(stop, begin) - begin:] = 0
         if inj is not None and inj[0] == r and begin <= inj[1] < end:
             g[inj[1] - begin] = POS_INF[wl.dtype] if inj[2] == "inf" else QNAN[wl.dtype]
         out.append(g)

@@ -1,0 +1,240 @@
+"""Parity at the benchmark sizes, in the launch configuration bench.py times.
+
+* LLaMA-7B-shaped owner-0 shard (842,301,952 elements, N = 8 bf16 ranks, clip
+  1.0, 5 steps) and LLaMA-70B-shaped owner-0 shard (8,622,081,024 elements,
+  in-place reduce into rank 0's buffer, 3 steps), with the same resident
+  gradient batch every step as in the bench.  The oracle recomputes the
+  overflow flag and the squared norm of the whole shard on the host
+  (regenerating all N ranks' gradients chunk by chunk), and follows sampled
+  element chunks (partition ends, tensor starts, random places) through every
+  step one by one: reduced gradient bit-exact, flag exact, norm within 1e-5,
+  master / m / v within 2e-6 relative (or bit-equal), 16-bit copy within 1 ulp.
+* The 10,000-tensor fragmented-bucket buffer (1,084,742,528 padded elements,
+  all 16 owners, 3 bucket windows, dynamic loss scaling, inf/NaN every 4th step,
+  40 steps, no clipping).  The global overflow flag follows from a property
+  that holds at any size -- every non-injected sum is bounded by
+  16 x (largest generated value) < 65504, so it is finite -- plus the oracle's
+  own reduce of the injected element; the norm is checked against a full host
+  recomputation on two steps; sampled chunks (owner and bucket boundaries,
+  every injected index, random places) are followed through all 40 steps.
+"""
+import gc
+import math
+import os
+import threading
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import inputs as I
+from synth import workloads as W
+import zero_partitioned_mixed_shard_amd as Z
+from zero_partitioned_mixed_shard_amd.shard import ShardStep
+from _common import (REL_TOL_NORM, assert_bits16_equal, assert_f32_close, assert_p16_close,
+                     to_np16, to_np32)
+
+pytestmark = pytest.mark.gpu
+
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+CHUNK = 1 << 23
+SAMPLE = 1024
+
+
+def _free_device_memory():
+    gc.collect()
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    return free
+
+
+def host_full_check(wl, begin, end, padded, step, scale):
+    """Oracle (flag, sumsq) of the reduced gradient over [begin, end)."""
+    local = threading.local()
+
+    def work(rg):
+        a, b = rg
+        if not hasattr(local, "bufs"):
+            local.bufs = [np.empty(CHUNK, np.uint16) for _ in range(wl.world)]
+            local.red = np.empty(CHUNK, np.uint16)
+        g = I.host_rank_grads(wl, step, scale, a, b, padded, out_bufs=local.bufs)
+        red = oracle.reduce(g, wl.dtype, out=local.red[:b - a])
+        return oracle.check(red, wl.dtype, 1.0 / scale)
+
+    ranges = [(a, min(end, a + CHUNK)) for a in range(begin, end, CHUNK)]
+    with ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(work, ranges))
+    return max(p[0] for p in parts), math.fsum(p[1] for p in parts)
+
+
+def sample_chunks(wl, offs, begin, end, extra=(), n_random=32, seed=0):
+    rng = np.random.default_rng(seed)
+    starts = {begin, end - SAMPLE}
+    inside = offs[(offs >= begin) & (offs < end - SAMPLE)]
+    for o in list(inside[:3]) + list(rng.choice(inside, min(8, inside.size), replace=False)):
+        starts.add(int(o))
+        if o - SAMPLE // 2 >= begin:
+            starts.add(int(o) - SAMPLE // 2)          # straddles a tensor start
+    for x in extra:
+        starts.add(int(max(begin, min(end - SAMPLE, x - SAMPLE // 2))))
+    starts |= {int(x) for x in rng.integers(begin, end - SAMPLE, n_random)}
+    out = []
+    for s in sorted(starts):                          # merge overlapping chunks
+        if out and s <= out[-1][1]:
+            out[-1] = (out[-1][0], max(out[-1][1], s + SAMPLE))
+        else:
+            out.append((s, s + SAMPLE))
+    return out
+
+
+def gather(t, chunks, base):
+    return torch.cat([t[a - base:b - base] for a, b in chunks])
+
+
+class SampledOracle:
+    """Oracle state of the sampled chunks, stepped element by element."""
+
+    def __init__(self, wl, offs, chunks):
+        self.wl, self.chunks = wl, chunks
+        self.states = [oracle.OwnerState.from_param16(I.host_param16(wl, offs, a, b), wl.dtype)
+                       for a, b in chunks]
+        self.hp = oracle.HParams(wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, wl.clip)
+
+    def step(self, gen_step, scale, padded, flag, sumsq, t):
+        reds = []
+        for (a, b), st in zip(self.chunks, self.states):
+            g = I.host_rank_grads(self.wl, gen_step, scale, a, b, padded)
+            red = oracle.reduce(g, self.wl.dtype)
+            reds.append(red)
+            oracle.adamw(st.master, st.exp_avg, st.exp_avg_sq, st.param16, red, self.wl.dtype,
+                         1.0 / scale, sumsq, flag, self.hp, t)
+        return np.concatenate(reds)
+
+    def compare(self, shard, red_dev, base, where):
+        assert_bits16_equal(to_np16(red_dev), self.red_cat, self.wl.dtype, where + " reduce")
+        want = {k: np.concatenate([getattr(s, k) for s in self.states])
+                for k in ("master", "exp_avg", "exp_avg_sq", "param16")}
+        u = [assert_f32_close(to_np32(gather(shard.master, self.chunks, base)), want["master"],
+                              where + " master"),
+             assert_f32_close(to_np32(gather(shard.exp_avg, self.chunks, base)), want["exp_avg"],
+                              where + " exp_avg"),
+             assert_f32_close(to_np32(gather(shard.exp_avg_sq, self.chunks, base)),
+                              want["exp_avg_sq"], where + " exp_avg_sq")]
+        assert_p16_close(to_np16(gather(shard.param16, self.chunks, base)), want["param16"],
+                         self.wl.dtype, where + " param16")
+        return u
+
+
+@pytest.mark.parametrize("name", ["llama7b", "llama70b"])
+def test_llama_shard_fullsize_sampled(name):
+    wl = W.WORKLOADS[name]
+    offs, parts, padded = oracle.layout(wl.numels, wl.world, wl.align)
+    begin, end = int(parts[0]), int(parts[1])
+    count = end - begin
+    in_place = name == "llama70b"
+    need = count * (12 + 2 + (0 if in_place else 2) + 2 * wl.world) + (1 << 30)
+    free = _free_device_memory()
+    if free < need:
+        pytest.skip(f"{name}: needs {need / 1e9:.1f} GB of device memory, {free / 1e9:.1f} GB free")
+    t0 = time.time()
+    print(f"{name}: {count} owned elements, {wl.world} ranks, in_place={in_place}", flush=True)
+    shard = ShardStep(begin, end, [(begin, end)], wl.dtype, lr=wl.lr, beta1=wl.beta1,
+                      beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
+                      max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
+                      window=wl.window, in_place_rank=0 if in_place else None)
+    shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16))
+    bufs = [I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded) for r in range(wl.world)]
+    torch.cuda.synchronize()
+    flag_o, sumsq_o = host_full_check(wl, begin, end, padded, 1, wl.scale0)
+    print(f"{name}: oracle full-shard norm {math.sqrt(sumsq_o):.9g} ({time.time() - t0:.1f} s)",
+          flush=True)
+    chunks = sample_chunks(wl, offs, begin, end)
+    so = SampledOracle(wl, offs, chunks)
+    t = 0
+    try:
+        for s in range(1, wl.steps + 1):
+            if in_place and s > 1:       # rank 0's buffer holds last step's sum
+                I.device_rank_grad(wl, 1, wl.scale0, 0, begin, end, padded, out=bufs[0])
+            info = shard.step(bufs)
+            t += 1
+            so.red_cat = so.step(1, wl.scale0, padded, flag_o, sumsq_o, t)
+            where = f"{name} step {s}"
+            assert info.overflow == flag_o == 0, where
+            rel = abs(math.sqrt(info.sumsq) - math.sqrt(sumsq_o)) / math.sqrt(sumsq_o)
+            assert rel <= REL_TOL_NORM, (where, rel)
+            ulps = so.compare(shard, gather(shard.reduced(bufs), chunks, begin), begin, where)
+            print(f"{where}: norm rel diff {rel:.2e}, sampled {sum(b - a for a, b in chunks)} "
+                  f"elements in {len(chunks)} chunks, "
+                  f"max-ulp(master,m,v)={ulps} ({time.time() - t0:.1f} s)", flush=True)
+    finally:
+        del shard, bufs
+        _free_device_memory()
+
+
+def test_buckets_fullsize_all_owners_sampled():
+    wl = W.WORKLOADS["buckets"]
+    offs, parts, padded = oracle.layout(wl.numels, wl.world, wl.align)
+    first = oracle.buckets(wl.numels, wl.bucket_cap)
+    windows = W.bucket_windows(wl, offs, padded, first)
+    owners = [(int(parts[p]), int(parts[p + 1])) for p in range(wl.world)]
+    need = padded * (12 + 2 + 2 + 2 * wl.world) + (1 << 30)
+    free = _free_device_memory()
+    if free < need:
+        pytest.skip(f"needs {need / 1e9:.1f} GB of device memory, {free / 1e9:.1f} GB free")
+    inj = W.injections(wl, padded)
+    # property: without an injection every reduced value is finite, at every scale used
+    scale = wl.scale0
+    while scale >= wl.min_scale:
+        assert wl.world * wl.grad_spec(scale).max_abs < 65504.0
+        scale /= 2
+    t0 = time.time()
+    shard = ShardStep(0, padded, owners, wl.dtype, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
+                      eps=wl.eps, weight_decay=wl.weight_decay, max_grad_norm=wl.clip,
+                      scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window,
+                      windows=windows)
+    shard.load_param16(I.device_param16(wl, offs, 0, padded, out=shard.param16))
+    bufs = [torch.empty(padded, dtype=shard.tdtype, device="cuda") for _ in range(wl.world)]
+    extra = [p for p, _ in owners[1:]] + [a for a, _ in windows[1:]] + [v[1] for v in inj.values()]
+    chunks = sample_chunks(wl, offs, 0, padded, extra=extra, n_random=24, seed=5)
+    so = SampledOracle(wl, offs, chunks)
+    scaler = oracle.Scaler(wl.scale0, wl.min_scale, wl.window)
+    t = 0
+    try:
+        for s in range(1, wl.steps + 1):
+            scale = scaler.scale
+            assert shard.scale == scale
+            for r in range(wl.world):
+                I.device_rank_grad(wl, s, scale, r, 0, padded, padded, out=bufs[r])
+            info = shard.step(bufs)
+            # oracle flag: the injected element, reduced by the oracle; finite elsewhere
+            flag = 0
+            if s in inj:
+                r_inj, idx, _ = inj[s]
+                col = I.host_rank_grads(wl, s, scale, idx, idx + 1, padded)
+                flag = int(not np.isfinite(oracle.decode16(oracle.reduce(col, wl.dtype),
+                                                           wl.dtype)[0]))
+                assert flag == 1
+            where = f"buckets step {s}"
+            assert info.overflow == flag, where
+            if not flag:
+                t += 1
+            so.red_cat = so.step(s, scale, padded, flag, 0.0, t)
+            if s in (1, 13):
+                f_full, sumsq_full = host_full_check(wl, 0, padded, padded, s, scale)
+                assert f_full == 0
+                rel = abs(math.sqrt(info.sumsq) - math.sqrt(sumsq_full)) / math.sqrt(sumsq_full)
+                assert rel <= REL_TOL_NORM, (where, rel)
+                print(f"{where}: full norm rel diff {rel:.2e}", flush=True)
+            ulps = so.compare(shard, gather(shard.reduced(bufs), chunks, 0), 0, where)
+            scaler.update(flag)
+            assert shard.scale == scaler.scale and shard.t == t, where
+            print(f"{where}: overflow={info.overflow} scale={scale:g} t={t} "
+                  f"max-ulp={ulps} ({time.time() - t0:.1f} s)", flush=True)
+        assert scaler.scale == 64.0 and scaler.skipped == 10 and t == 30
+    finally:
+        del shard, bufs
+        _free_device_memory()

@@ -83,7 +83,10 @@ class ShardStep:
 
     # ---------------------------------------------------------------- state
     def load_param16(self, param16: torch.Tensor) -> None:
-        self.param16.copy_(param16)
+        """Initial state: the 16-bit copy, fp32 master = its float, m = v = 0.
+        `param16` may be self.param16 itself (filled in place)."""
+        if param16.data_ptr() != self.param16.data_ptr():
+            self.param16.copy_(param16)
         zero_init_master(self.master, self.param16)
         self.exp_avg.zero_()
         self.exp_avg_sq.zero_()
