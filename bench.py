@@ -8,10 +8,12 @@ already resident in HBM:
 Algorithmic HBM bytes per owned element: 2N + 2 for reduce+check (2N + 4 with
 --unfused, which re-reads the reduced gradient), 28 for AdamW.
 
-Default workload: owner 0's partition of the LLaMA-7B-shaped flat buffer
-(6,738,415,616 parameters, N = 8 ranks, 842,301,952 owned elements, bf16
+Default workload: owner 0's partition of the LLaMA-70B-shaped flat buffer
+(68,976,648,192 parameters, N = 8 ranks, 8,622,081,024 owned elements, bf16
 gradients N(0, 1e-4), AdamW lr 1e-3, betas (0.9, 0.999), eps 1e-8, wd 0.01,
-clip 1.0).
+clip 1.0), the largest configuration that fits one GPU: 258.7 GB resident,
+the reduce writing in place into rank 0's buffer.  --workload llama7b runs the
+LLaMA-7B-shaped shard (842,301,952 owned elements, separate reduced buffer).
 
 Prints one JSON line: params updated per second (owned elements x applied
 steps / time), per-phase times measured with HIP events on the stream the
@@ -32,18 +34,20 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "zero_partitioned_mixed_shard_amd", "csrc", "zero_shard.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "adamw_reduce_llama7b_hbm_counters.md")
+COUNTERS = {w: os.path.join(ROOT, "profiles", f"adamw_reduce_{w}_hbm_counters.md")
+            for w in ("llama7b", "llama70b")}
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    or None when the kernel source changed since the counters were taken."""
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary, or None when there is none or the kernel source changed
+    since the counters were taken."""
     import hashlib
     import re
     try:
         src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-        text = open(COUNTERS).read()
-    except OSError:
+        text = open(COUNTERS[workload]).read()
+    except (OSError, KeyError):
         return None
     m = re.search(rf"machine-readable: {kernel} traffic_bytes=(\d+) source_sha256_16=(\w+)", text)
     if not m or m.group(2) != src:
@@ -56,7 +60,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama7b",
+    ap.add_argument("--workload", default="llama70b",
                     choices=["toy", "bert", "llama7b", "llama70b"])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (e.g. under a profiler)")
@@ -66,6 +70,10 @@ def parse():
                     help="also run a plain device copy of this size (for HBM counter scaling)")
     ap.add_argument("--unfused", action="store_true",
                     help="separate reduce and check calls instead of the fused one")
+    ap.add_argument("--no-arena", action="store_true",
+                    help="separate allocations instead of one arena with spread placement")
+    ap.add_argument("--min-gap-gib", type=float, default=0.0,
+                    help="minimum distance between the AdamW streams' bases in the arena")
     return ap.parse_args()
 
 
@@ -125,6 +133,32 @@ def cpu_baseline(wl, begin: int, seconds: float) -> dict:
                       f"on {threads} threads"}
 
 
+def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
+    """Owner 0's shard of `wl` as the bench runs it: state, reduced gradient
+    and the N rank buffers (the LLaMA-70B shard reduces in place into rank 0's
+    buffer), initial 16-bit weights and one gradient batch generated on the
+    device.  Returns (shard, begin, end, padded, in_place)."""
+    import torch
+
+    from synth import inputs as I
+    import zero_partitioned_mixed_shard_amd as Z
+    from zero_partitioned_mixed_shard_amd.shard import ShardStep
+
+    offs, parts, padded = Z.zero_partition_layout(wl.numels, wl.world, wl.align)
+    begin, end = int(parts[0]), int(parts[1])
+    in_place = wl.name == "llama70b"       # 8 rank buffers + state fill ~259 GB
+    shard = ShardStep(begin, end, [(begin, end)], wl.dtype, lr=wl.lr, beta1=wl.beta1,
+                      beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
+                      max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
+                      window=wl.window, in_place_rank=0 if in_place else None, fused=fused,
+                      own_ranks=True, world=wl.world, arena=arena, min_gap=min_gap)
+    shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16))
+    for r, buf in enumerate(shard.rank_bufs):
+        I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded, out=buf)
+    torch.cuda.synchronize()
+    return shard, begin, end, padded, in_place
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -141,19 +175,6 @@ def main():
 
     wl = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    offs, parts, padded = Z.zero_partition_layout(wl.numels, wl.world, wl.align)
-    begin, end = int(parts[0]), int(parts[1])
-    count = end - begin
-    in_place = args.workload == "llama70b"       # 8 rank buffers + state fill ~259 GB
-    shard = ShardStep(begin, end, [(begin, end)], wl.dtype, lr=wl.lr, beta1=wl.beta1,
-                      beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
-                      max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
-                      window=wl.window, in_place_rank=0 if in_place else None,
-                      fused=not args.unfused)
-    shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16))
-    bufs = [I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded) for r in range(wl.world)]
-    torch.cuda.synchronize()
-
     if args.copy_calibration_gib > 0:
         # one elementwise kernel that reads and writes exactly `nbytes` each:
         # the reference for scaling the HBM byte counters
@@ -164,6 +185,13 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+        torch.cuda.empty_cache()
+    shard, begin, end, padded, in_place = build_shard(
+        wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
+        fused=not args.unfused)
+    count = end - begin
+    bufs = shard.rank_bufs
+
 
     for _ in range(args.warmup):
         Z.zero_partition_layout(wl.numels, wl.world, wl.align)
@@ -210,7 +238,7 @@ def main():
     step_bytes = sum(bytes_per.values()) * count
     adam_avg_s = float(np.mean(ms["adamw"])) * 1e-3
     achieved = 28 * count / adam_avg_s / 1e9
-    traffic = measured_traffic("adamw_kernel") if args.workload == "llama7b" else None
+    traffic = measured_traffic("adamw_kernel", args.workload)
 
     result = {
         "metric": "params updated/s per GPU (ZeRO shard AdamW step) + achieved HBM GB/s % of peak",
@@ -234,6 +262,9 @@ def main():
             "clip": wl.clip,
             "in_place_reduce": in_place,
             "fused_reduce_check": not args.unfused,
+            "placement": ("separate allocations" if args.no_arena else
+                          f"one arena, AdamW streams interleaved with rank buffers, "
+                          f"min gap {args.min_gap_gib:g} GiB"),
             "parallelism": "one owner partition on one GPU (N ranks simulated in HBM)",
         },
         "step_GBps": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
@@ -254,7 +285,7 @@ def main():
                             "factors from a known-size elementwise kernel)",
         },
     }
-    del bufs
+    del bufs, shard
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, begin, args.cpu_seconds)

@@ -29,6 +29,7 @@ import numpy as np
 import pytest
 import torch
 
+import bench
 import oracle
 import synth
 from synth import inputs as I
@@ -142,13 +143,8 @@ def test_llama_shard_fullsize_sampled(name):
         pytest.skip(f"{name}: needs {need / 1e9:.1f} GB of device memory, {free / 1e9:.1f} GB free")
     t0 = time.time()
     print(f"{name}: {count} owned elements, {wl.world} ranks, in_place={in_place}", flush=True)
-    shard = ShardStep(begin, end, [(begin, end)], wl.dtype, lr=wl.lr, beta1=wl.beta1,
-                      beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
-                      max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
-                      window=wl.window, in_place_rank=0 if in_place else None)
-    shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16))
-    bufs = [I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded) for r in range(wl.world)]
-    torch.cuda.synchronize()
+    shard, _, _, _, _ = bench.build_shard(wl)        # exactly as bench.py runs it
+    bufs = shard.rank_bufs
     flag_o, sumsq_o = host_full_check(wl, begin, end, padded, 1, wl.scale0)
     print(f"{name}: oracle full-shard norm {math.sqrt(sumsq_o):.9g} ({time.time() - t0:.1f} s)",
           flush=True)
