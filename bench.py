@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama70b",
-                    choices=["toy", "bert", "llama7b", "llama70b"])
+                    choices=["toy", "bert", "llama7b", "llama70b", "buckets"])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (e.g. under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=2.0,
@@ -159,6 +159,51 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
     return shard, begin, end, padded, in_place
 
 
+def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
+    """The 10,000-tensor group with all N owners on this GPU, as the bench runs
+    it: rank 0's gradient arrives as one separate device tensor per parameter
+    (10,000 allocations) and is copied into rank 0's flat buffer bucket by
+    bucket (zero_flat_gather, ZeRO-2 source walkthrough section 2.4
+    contiguous_gradients); ranks 1..N-1 arrive already flat.  Returns
+    (shard, copy_in, padded) where copy_in() enqueues the copy-in."""
+    import torch
+
+    from synth import inputs as I
+    from synth import workloads as W
+    import zero_partitioned_mixed_shard_amd as Z
+    from zero_partitioned_mixed_shard_amd.shard import ShardStep
+
+    offs, parts, padded = Z.zero_partition_layout(wl.numels, wl.world, wl.align)
+    first = Z.zero_bucket_layout(wl.numels, wl.bucket_cap)
+    windows = W.bucket_windows(wl, offs, padded, first)
+    owners = [(int(parts[p]), int(parts[p + 1])) for p in range(wl.world)]
+    shard = ShardStep(0, padded, owners, wl.dtype, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
+                      eps=wl.eps, weight_decay=wl.weight_decay, max_grad_norm=wl.clip,
+                      scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window,
+                      windows=windows, fused=fused, own_ranks=True, world=wl.world,
+                      arena=arena, min_gap=min_gap)
+    shard.load_param16(I.device_param16(wl, offs, 0, padded, out=shard.param16))
+    for r, buf in enumerate(shard.rank_bufs):
+        I.device_rank_grad(wl, 1, wl.scale0, r, 0, padded, padded, out=buf)
+    # rank 0's gradient as per-parameter tensors holding the same values
+    flat0 = shard.rank_bufs[0]
+    grads = [flat0[int(o):int(o) + int(n)].clone() for o, n in zip(offs, wl.numels)]
+    flat0.fill_(-1.0)                       # the copy-in must rewrite every element
+    tables = []
+    for b, (a, z) in enumerate(windows):
+        ks = range(int(first[b]), int(first[b + 1]))
+        tables.append((a, z, Z.tensor_descs([grads[k] for k in ks], [int(offs[k]) - a for k in ks])))
+
+    def copy_in():
+        for a, z, descs in tables:
+            Z.zero_flat_gather(flat0[a:z], descs)
+
+    copy_in()
+    torch.cuda.synchronize()
+    shard.per_tensor_grads = grads
+    return shard, copy_in, padded
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -186,19 +231,28 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
-    shard, begin, end, padded, in_place = build_shard(
-        wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
-        fused=not args.unfused)
+    copy_in = None
+    if args.workload == "buckets":
+        shard, copy_in, padded = build_buckets(wl, arena=not args.no_arena,
+                                               min_gap=int(args.min_gap_gib * 2 ** 30),
+                                               fused=not args.unfused)
+        begin, end, in_place = 0, padded, False
+    else:
+        shard, begin, end, padded, in_place = build_shard(
+            wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
+            fused=not args.unfused)
     count = end - begin
     bufs = shard.rank_bufs
 
 
     for _ in range(args.warmup):
         Z.zero_partition_layout(wl.numels, wl.world, wl.align)
+        if copy_in:
+            copy_in()
         shard.step(bufs)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     applied = 0
     infos = []
     torch.cuda.synchronize()
@@ -208,6 +262,9 @@ def main():
     start.record()
     for k in range(args.steps):
         Z.zero_partition_layout(wl.numels, wl.world, wl.align)
+        ev[k][4].record()
+        if copy_in:
+            copy_in()
         info = shard.step(bufs, marks=ev[k])
         applied += info.applied
         infos.append(info)
@@ -229,6 +286,9 @@ def main():
             ms["reduce_check"].append(e[0].elapsed_time(e[2]))
             ms["adamw"].append(e[2].elapsed_time(e[3]))
         bytes_per = {"reduce_check": 2 * wl.world + 2, "adamw": 28}
+    if copy_in:
+        ms["copy_in"] = [e[4].elapsed_time(e[0]) for e in ev]
+        bytes_per["copy_in"] = 4
     phases = {}
     for k, v in ms.items():
         avg = float(np.mean(v))
@@ -254,7 +314,8 @@ def main():
         "dtype": "fp32",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}-shaped owner-0 shard",
+            "workload": (f"{wl.name}-shaped owner-0 shard" if args.workload != "buckets" else
+                         "10,000-tensor group, all owners, copy-in + bucketed reduce + AdamW"),
             "description": wl.description,
             "owned_elems": count,
             "ranks": wl.world,

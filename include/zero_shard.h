@@ -90,6 +90,15 @@ typedef struct zero_loss_scaler {
     int64_t skipped;    /* total steps skipped for overflow               */
 } zero_loss_scaler;
 
+/* One tensor of a flattened group (device array of these, sorted by offset,
+ * for zero_flat_gather / zero_flat_scatter).  32 bytes. */
+typedef struct zero_tensor_desc {
+    void* ptr;          /* device pointer to the tensor's `numel` 16-bit values   */
+    int64_t offset;     /* index of the tensor's first element in the flat buffer */
+    int64_t numel;      /* elements                                               */
+    int64_t reserved;   /* set to 0                                               */
+} zero_tensor_desc;
+
 /* ---------------------------------------------------------------- host ---- */
 
 /* Flatten + align + partition (ZeRO-2 source walkthrough, section 4.1 steps
@@ -148,6 +157,32 @@ const char* zero_status_str(int status);
  *   param16[count]  device, in  (16-bit patterns of `dtype`) */
 int zero_init_master(float* master, const void* param16, int64_t count, int32_t dtype,
                      hipStream_t stream);
+
+/* Bucket copy-in (ZeRO-2 source walkthrough section 2.4: with
+ * contiguous_gradients each gradient is copied into one contiguous buffer;
+ * section 4.2: each ready gradient goes into the reduce bucket at its place in
+ * the flattened group):
+ *   flat[d.offset + j] = d.ptr[j] for every descriptor d and j < d.numel;
+ *   every flat element in [0, flat_count) that no descriptor covers is set to 0
+ *   (the alignment padding).
+ *   flat[flat_count]   device, out, 16-bit patterns (copied unchanged)
+ *   descs[n_descs]     device array, sorted by offset, ranges disjoint and
+ *                      inside [0, flat_count); each ptr valid for numel values.
+ * The kernel reads a tensor only at indices below its numel and writes the
+ * flat buffer only below flat_count, so a table that breaks the ordering rule
+ * gives wrong values but no out-of-range access.
+ * Errors: ZERO_EINVAL for flat_count < 0, n_descs < 0, or a NULL pointer with
+ * a nonzero count. */
+int zero_flat_gather(void* flat, int64_t flat_count, const zero_tensor_desc* descs,
+                     int64_t n_descs, hipStream_t stream);
+
+/* Write-back of an updated flat 16-bit buffer into its tensors (ZeRO-2 source
+ * walkthrough section 4.4: after the step the updated partitions are gathered
+ * back into the full parameters):  d.ptr[j] = flat[d.offset + j] for every
+ * descriptor d and j < d.numel.  Arguments as for zero_flat_gather; flat is
+ * read only. */
+int zero_flat_scatter(const void* flat, int64_t flat_count, const zero_tensor_desc* descs,
+                      int64_t n_descs, hipStream_t stream);
 
 /* Reduce to the owner: dst[i] = round16(g_0[i] + g_1[i] + ... + g_{N-1}[i]),
  * the additions done in fp64 in rank order and the result rounded once to

@@ -96,9 +96,12 @@ def lib():
         L.oracle_adamw_f64.argtypes = [P, P, P, P, i64, i32, f64, f64, P, P, P, P]
         L.oracle_init_master.argtypes = [P, P, i64, i32]
         L.oracle_scaler_update.argtypes = [P, ctypes.c_uint32]
+        L.oracle_flat_gather.argtypes = [P, i64, P, P, P, i64]
+        L.oracle_flat_scatter.argtypes = [P, P, P, P, i64]
         for name in ("oracle_decode16", "oracle_encode16_from_f32", "oracle_encode16_from_f64",
                      "oracle_reduce", "oracle_check", "oracle_adam_consts_for", "oracle_adamw",
-                     "oracle_adamw_f64", "oracle_init_master", "oracle_scaler_update"):
+                     "oracle_adamw_f64", "oracle_init_master", "oracle_scaler_update",
+                     "oracle_flat_gather", "oracle_flat_scatter"):
             getattr(L, name).restype = None
         _lib = L
     return _lib
@@ -157,6 +160,32 @@ def buckets(numels: Sequence[int], cap: int) -> np.ndarray:
     if rc != OK:
         raise ValueError(f"oracle_buckets: status {rc}")
     return first[:int(nb[0]) + 1].copy()
+
+
+# --------------------------------------------------------------------------
+# Bucket copy-in (gather into the flat buffer) and write-back (scatter out)
+# --------------------------------------------------------------------------
+def flat_gather(tensors: Sequence[np.ndarray], offsets: Sequence[int], flat_count: int) -> np.ndarray:
+    ts = [np.ascontiguousarray(t, dtype=np.uint16) for t in tensors]
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    numel = np.array([t.size for t in ts], dtype=np.int64)
+    assert offs.size == len(ts)
+    assert all(o >= 0 and o + n <= flat_count for o, n in zip(offs, numel))
+    ptrs = (ctypes.c_void_p * max(1, len(ts)))(*[_p(t) for t in ts])
+    flat = np.empty(flat_count, dtype=np.uint16)
+    lib().oracle_flat_gather(_p(flat), flat_count, ptrs, _p(offs), _p(numel), len(ts))
+    return flat
+
+
+def flat_scatter(flat: np.ndarray, offsets: Sequence[int], numels: Sequence[int]) -> list:
+    flat = np.ascontiguousarray(flat, dtype=np.uint16)
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    numel = np.ascontiguousarray(numels, dtype=np.int64)
+    assert all(o >= 0 and o + n <= flat.size for o, n in zip(offs, numel))
+    outs = [np.empty(int(n), dtype=np.uint16) for n in numel]
+    ptrs = (ctypes.c_void_p * max(1, len(outs)))(*[_p(t) for t in outs])
+    lib().oracle_flat_scatter(_p(flat), ptrs, _p(offs), _p(numel), len(outs))
+    return outs
 
 
 # --------------------------------------------------------------------------

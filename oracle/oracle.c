@@ -197,6 +197,31 @@ int oracle_buckets(const int64_t* numel, int64_t n_tensors, int64_t cap,
 }
 
 /* ------------------------------------------------------------------------- */
+/* Bucket copy-in and write-back.                                            */
+/* ZeRO-2 source walkthrough (discosf.com) section 2.4: with                  */
+/* contiguous_gradients the gradients are copied into one contiguous buffer;  */
+/* section 4.2: each ready gradient goes into the reduce bucket at its place  */
+/* in the flattened group; section 4.4: after the step the updated partitions */
+/* are gathered back into the full parameters.                                */
+/* gather:  flat[offset[k] + j] = tensor_k[j] for j < numel[k]; every flat    */
+/*          element that no tensor covers becomes 0.                          */
+/* scatter: tensor_k[j] = flat[offset[k] + j] for j < numel[k].               */
+/* Elements are copied as 16-bit patterns, unchanged.                         */
+/* ------------------------------------------------------------------------- */
+void oracle_flat_gather(uint16_t* flat, int64_t flat_count, const uint16_t* const* tensors,
+                        const int64_t* offset, const int64_t* numel, int64_t n_tensors) {
+    for (int64_t i = 0; i < flat_count; ++i) flat[i] = 0;
+    for (int64_t k = 0; k < n_tensors; ++k)
+        for (int64_t j = 0; j < numel[k]; ++j) flat[offset[k] + j] = tensors[k][j];
+}
+
+void oracle_flat_scatter(const uint16_t* flat, uint16_t* const* tensors, const int64_t* offset,
+                         const int64_t* numel, int64_t n_tensors) {
+    for (int64_t k = 0; k < n_tensors; ++k)
+        for (int64_t j = 0; j < numel[k]; ++j) tensors[k][j] = flat[offset[k] + j];
+}
+
+/* ------------------------------------------------------------------------- */
 /* Reduce: red[i] = the sum over ranks r = 0..N-1 of g_r[i], rounded once to   */
 /* the 16-bit communication type.  ZeRO 优化器, "ZeRO Stage 1": after the      */
 /* reduce the owner holds the sum of every rank's gradient.  ZeRO-2 source     */

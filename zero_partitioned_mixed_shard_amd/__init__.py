@@ -46,7 +46,7 @@ EXPORTS = (
     "zero_partition_layout", "zero_bucket_layout", "zero_memory_bytes",
     "zero_loss_scaler_update", "zero_status_str", "zero_init_master", "zero_reduce_owned",
     "zero_check_workspace_bytes", "zero_unscale_check_norm", "zero_reduce_check_owned",
-    "zero_adamw_step",
+    "zero_adamw_step", "zero_flat_gather", "zero_flat_scatter",
 )
 
 
@@ -87,6 +87,8 @@ def _load():
         "zero_reduce_check_owned": ([P, P, i32, i64, i32, f32, P, P, ctypes.c_size_t, i32, P],
                                     ctypes.c_int),
         "zero_adamw_step": ([P, P, P, P, P, i64, i32, P, P, P], ctypes.c_int),
+        "zero_flat_gather": ([P, i64, P, i64, P], ctypes.c_int),
+        "zero_flat_scatter": ([P, i64, P, i64, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -248,6 +250,36 @@ def zero_adamw_step(master, exp_avg, exp_avg_sq, param16, grad16, hp: zero_adamw
                                 _dev(param16, 2, count, "param16"), _dev(grad16, 2, count, "grad16"),
                                 count, dt, ctypes.byref(hp), res.data_ptr(), _stream(stream)),
            "zero_adamw_step")
+
+
+def tensor_descs(tensors: Sequence, offsets: Sequence[int], device="cuda"):
+    """Device table of zero_tensor_desc (int64 [n, 4]: ptr, offset, numel, 0)
+    for 16-bit device tensors placed at `offsets` of a flat buffer."""
+    import torch
+    rows = []
+    for t, off in zip(tensors, offsets):
+        if t.numel() and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if t.numel() and t.element_size() != 2:
+            raise ValueError("16-bit tensors expected")
+        rows.append((t.data_ptr() if t.numel() else 0, int(off), t.numel(), 0))
+    host = torch.tensor(rows if rows else [(0, 0, 0, 0)], dtype=torch.int64)
+    return host[:len(rows)].to(device)
+
+
+def zero_flat_gather(flat, descs, count: Optional[int] = None, stream=None) -> None:
+    """descs: device int64 [n, 4] table from tensor_descs()."""
+    count = flat.numel() if count is None else count
+    _check(_lib.zero_flat_gather(_dev(flat, 2, count, "flat"), count,
+                                 descs.data_ptr() if descs.numel() else None, descs.shape[0],
+                                 _stream(stream)), "zero_flat_gather")
+
+
+def zero_flat_scatter(flat, descs, count: Optional[int] = None, stream=None) -> None:
+    count = flat.numel() if count is None else count
+    _check(_lib.zero_flat_scatter(_dev(flat, 2, count, "flat"), count,
+                                  descs.data_ptr() if descs.numel() else None, descs.shape[0],
+                                  _stream(stream)), "zero_flat_scatter")
 
 
 def read_result(res) -> zero_step_result:
