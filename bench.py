@@ -70,6 +70,9 @@ def parse():
                     help="also run a plain device copy of this size (for HBM counter scaling)")
     ap.add_argument("--unfused", action="store_true",
                     help="separate reduce and check calls instead of the fused one")
+    ap.add_argument("--round-robin-owner", type=int, default=None,
+                    help="instead of flat partition 0, own the whole tensors i with "
+                         "i mod N == this owner (packed; one reduce window per tensor)")
     ap.add_argument("--no-arena", action="store_true",
                     help="separate allocations instead of one arena with spread placement")
     ap.add_argument("--min-gap-gib", type=float, default=0.0,
@@ -204,6 +207,45 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
     return shard, copy_in, padded
 
 
+def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fused: bool = True):
+    """Round-robin inter-tensor ownership (ZeRO 优化器, "参数分配策略"): this
+    owner holds the whole tensors i with i mod N == owner, packed back to back
+    (state only for what it owns); each tensor is reduced to it on its own
+    (one reduce window per tensor, as the per-parameter reduce of that page's
+    training loop).  Returns (shard, owned_elems, n_tensors, imbalance) where
+    imbalance = the largest owner's elements / the mean."""
+    import torch
+
+    from synth import inputs as I
+    from zero_partitioned_mixed_shard_amd.shard import ShardStep
+    import zero_partitioned_mixed_shard_amd as Z
+
+    offs, parts, padded = Z.zero_partition_layout(wl.numels, wl.world, wl.align)
+    owned = [i for i, n in enumerate(wl.numels) if i % wl.world == owner and n > 0]
+    sizes = [int(wl.numels[i]) for i in owned]
+    packed = [0]
+    for n in sizes:
+        packed.append(packed[-1] + n)
+    count = packed[-1]
+    per_owner = [sum(int(n) for i, n in enumerate(wl.numels) if i % wl.world == p)
+                 for p in range(wl.world)]
+    windows = [(packed[k], packed[k + 1]) for k in range(len(owned))]
+    shard = ShardStep(0, count, [(0, count)], wl.dtype, lr=wl.lr, beta1=wl.beta1,
+                      beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
+                      max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
+                      window=wl.window, windows=windows, fused=fused, own_ranks=True,
+                      world=wl.world, arena=arena, min_gap=min_gap)
+    for k, i in enumerate(owned):
+        a, b = packed[k], packed[k + 1]
+        g0 = int(offs[i])
+        I.device_param16(wl, offs, g0, g0 + sizes[k], out=shard.param16[a:b])
+        for r, buf in enumerate(shard.rank_bufs):
+            I.device_rank_grad(wl, 1, wl.scale0, r, g0, g0 + sizes[k], padded, out=buf[a:b])
+    shard.load_param16(shard.param16)
+    torch.cuda.synchronize()
+    return shard, count, len(owned), max(per_owner) / (sum(per_owner) / wl.world)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -232,7 +274,15 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     copy_in = None
-    if args.workload == "buckets":
+    rr_info = None
+    if args.round_robin_owner is not None:
+        shard, count_rr, n_owned, imbalance = build_round_robin(
+            wl, args.round_robin_owner, arena=not args.no_arena,
+            min_gap=int(args.min_gap_gib * 2 ** 30), fused=not args.unfused)
+        begin, end, padded, in_place = 0, count_rr, 0, False
+        rr_info = {"owner": args.round_robin_owner, "owned_tensors": n_owned,
+                   "owned_elems": count_rr, "largest_over_mean_owner": round(imbalance, 4)}
+    elif args.workload == "buckets":
         shard, copy_in, padded = build_buckets(wl, arena=not args.no_arena,
                                                min_gap=int(args.min_gap_gib * 2 ** 30),
                                                fused=not args.unfused)
@@ -315,7 +365,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{wl.name}-shaped owner-0 shard" if args.workload != "buckets" else
-                         "10,000-tensor group, all owners, copy-in + bucketed reduce + AdamW"),
+                         "10,000-tensor group, all owners, copy-in + bucketed reduce + AdamW")
+                        if rr_info is None else
+                        f"{wl.name}-shaped, round-robin owner {rr_info['owner']} (whole tensors)",
+            "round_robin": rr_info,
             "description": wl.description,
             "owned_elems": count,
             "ranks": wl.world,

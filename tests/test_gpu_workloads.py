@@ -25,10 +25,20 @@ from _common import (REL_TOL_NORM, assert_bits16_equal, assert_f32_close, assert
 pytestmark = pytest.mark.gpu
 
 
-def _setup(wl, owner_ids):
+def round_robin_ranges(wl, offs, owner):
+    """Tensors i with i mod N == owner, whole (ZeRO 优化器, "参数分配策略")."""
+    return [(int(offs[i]), int(offs[i]) + int(n)) for i, n in enumerate(wl.numels)
+            if i % wl.world == owner and n > 0]
+
+
+def _setup(wl, owner_ids, round_robin=False):
     offs, parts, padded = oracle.layout(wl.numels, wl.world, wl.align)
     d_offs, d_parts, d_padded = Z.zero_partition_layout(wl.numels, wl.world, wl.align)
     assert np.array_equal(offs, d_offs) and np.array_equal(parts, d_parts) and padded == d_padded
+    if round_robin:
+        owners = [r for p in owner_ids for r in round_robin_ranges(wl, offs, p)]
+        owners.sort()
+        return offs, padded, owners, 0, wl.phi, None
     owners = [(int(parts[p]), int(parts[p + 1])) for p in owner_ids]
     begin, end = owners[0][0], owners[-1][1]
     windows = None
@@ -39,10 +49,10 @@ def _setup(wl, owner_ids):
     return offs, padded, owners, begin, end, windows
 
 
-def run_parity(name, owner_ids, steps=None, threads=4, fused=True):
+def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=False):
     wl = W.WORKLOADS[name]
     steps = wl.steps if steps is None else steps
-    offs, padded, owners, begin, end, windows = _setup(wl, owner_ids)
+    offs, padded, owners, begin, end, windows = _setup(wl, owner_ids, round_robin)
     shard = ShardStep(begin, end, owners, wl.dtype, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
                       eps=wl.eps, weight_decay=wl.weight_decay, max_grad_norm=wl.clip,
                       scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window, windows=windows,
@@ -74,15 +84,18 @@ def run_parity(name, owner_ids, steps=None, threads=4, fused=True):
         skipped += not res.applied
         if not res.overflow:
             assert np.sqrt(info.sumsq) == pytest.approx(np.sqrt(res.sumsq), rel=REL_TOL_NORM), where
-        red = to_np16(shard.reduced(rank_bufs))
+        sel = np.concatenate([np.arange(a - begin, b - begin) for a, b in owners])
+        red = to_np16(shard.reduced(rank_bufs))[sel]
         assert_bits16_equal(red, np.concatenate(res.reduced), wl.dtype, where + " reduce")
         want = {k: np.concatenate([getattr(st, k) for st in states])
                 for k in ("master", "exp_avg", "exp_avg_sq", "param16")}
-        ulps = [assert_f32_close(to_np32(shard.master), want["master"], where + " master"),
-                assert_f32_close(to_np32(shard.exp_avg), want["exp_avg"], where + " exp_avg"),
-                assert_f32_close(to_np32(shard.exp_avg_sq), want["exp_avg_sq"],
+        ulps = [assert_f32_close(to_np32(shard.master)[sel], want["master"], where + " master"),
+                assert_f32_close(to_np32(shard.exp_avg)[sel], want["exp_avg"],
+                                 where + " exp_avg"),
+                assert_f32_close(to_np32(shard.exp_avg_sq)[sel], want["exp_avg_sq"],
                                  where + " exp_avg_sq")]
-        assert_p16_close(to_np16(shard.param16), want["param16"], wl.dtype, where + " param16")
+        assert_p16_close(to_np16(shard.param16)[sel], want["param16"], wl.dtype,
+                         where + " param16")
         print(f"{where}: overflow={info.overflow} norm={np.sqrt(info.sumsq):.6g} "
               f"max-ulp(master,m,v)={ulps}", flush=True)
     assert shard.scale == scaler.scale and shard.scaler.skipped == scaler.skipped == skipped
@@ -100,6 +113,20 @@ def test_toy_last_owner_with_padding():
 
 def test_bert_owner0_all_steps_clip():
     run_parity("bert", [0])
+
+
+@pytest.mark.parametrize("name,owner", [("toy", 0), ("toy", 5), ("bert", 3)])
+def test_round_robin_ownership(name, owner):
+    """Whole tensors i with i mod N == owner (ZeRO 优化器, "参数分配策略"):
+    one reduce+check call per owned tensor, accumulated into one norm, and one
+    AdamW call per owned tensor."""
+    run_parity(name, [owner], steps=4, round_robin=True)
+
+
+def test_round_robin_all_owners_equals_flat_union():
+    """Every owner under round-robin ownership together updates every tensor
+    exactly once: the same result as all owners of the flat layout."""
+    run_parity("toy_tiny", list(range(8)), steps=3, round_robin=True)
 
 
 @pytest.mark.parametrize("fused", [True, False])
