@@ -249,7 +249,7 @@ def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fuse
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the owner-shard step is "
+        print(json.dumps({"error": "runs on one GPU only: the owner-shard step is "
                           "measured on one GPU's partition; run with --gpus 1"}), file=sys.stderr)
         sys.exit(2)
     import numpy as np
