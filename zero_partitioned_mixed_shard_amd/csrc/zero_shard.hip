@@ -462,27 +462,70 @@ flat_gather_kernel(uint16_t* __restrict__ flat, Split s, const zero_tensor_desc*
     }
 }
 
-// Scatter: block b covers flat elements [b*2048, (b+1)*2048); lane l takes
-// elements b*2048 + l + 256*q, q = 0..7, so each wave instruction touches 64
-// consecutive 16-bit elements on both sides.
+// 8 consecutive 16-bit values (packed in w) to a 2-byte aligned address:
+// one 16-byte store when the address is 4-byte aligned, else a 16-bit store,
+// a 12-byte store and a 16-bit store.  Only these 16 bytes are written.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
+
+__device__ __forceinline__ void store8_unaligned(uint16_t* p, u32x4 w) {
+    if (((uintptr_t)p & 3) == 0) {
+        *reinterpret_cast<u32x4_a4*>(p) = w;
+        return;
+    }
+    p[0] = (uint16_t)(w[0] & 0xFFFFu);
+    u32x3_a4 mid;
+    mid[0] = __builtin_amdgcn_alignbit(w[1], w[0], 16);
+    mid[1] = __builtin_amdgcn_alignbit(w[2], w[1], 16);
+    mid[2] = __builtin_amdgcn_alignbit(w[3], w[2], 16);
+    *reinterpret_cast<u32x3_a4*>(p + 1) = mid;
+    p[7] = (uint16_t)(w[3] >> 16);
+}
+
+// Scatter: one 8-element tile of the flat buffer per lane (aligned through
+// the head split), the mirror of the gather.
 __global__ void __launch_bounds__(kThreads)
-flat_scatter_kernel(const uint16_t* __restrict__ flat, int64_t flat_count,
+flat_scatter_kernel(const uint16_t* __restrict__ flat, Split s,
                     const zero_tensor_desc* __restrict__ descs, int64_t n_descs) {
     __shared__ int64_t s_first;
-    const int64_t base = (int64_t)blockIdx.x * kTile;
-    if (threadIdx.x == 0) s_first = desc_at(descs, n_descs, base);
+    const int64_t base = s.aligned ? s.head + (int64_t)blockIdx.x * kTile
+                                   : (int64_t)blockIdx.x * kTile;
+    if (threadIdx.x == 0) s_first = desc_at(descs, n_descs, blockIdx.x == 0 ? 0 : base);
     __syncthreads();
     DescCursor cur;
     cur.d = descs;
     cur.n = n_descs;
     cur.load(s_first);
-#pragma unroll
-    for (int q = 0; q < kVec; ++q) {
-        const int64_t e = base + threadIdx.x + q * kThreads;
-        if (e >= flat_count) break;
-        cur.seek(e);
-        const int64_t j = cur.index(e);
-        if (j >= 0) cur.ptr[j] = flat[e];
+    const int64_t i = lane_tile();
+    const int64_t e0 = s.aligned ? s.head + i * kVec : i * kVec;
+    const bool vec_lane = s.aligned && i < s.nvec;
+    if (vec_lane || (!s.aligned && e0 < s.count)) {
+        cur.seek(e0);
+        const int64_t j0 = cur.index(e0);
+        if (vec_lane && j0 >= 0 && j0 + kVec <= cur.numel) {
+            store8_unaligned(cur.ptr + j0, load_nt(flat + e0));
+        } else {
+            for (int64_t e = e0; e < e0 + kVec && e < s.count; ++e) {
+                cur.seek(e);
+                const int64_t j = cur.index(e);
+                if (j >= 0) cur.ptr[j] = flat[e];
+            }
+        }
+    }
+    if (s.aligned && blockIdx.x == 0) {      // head and tail, one element per lane
+        const int t = threadIdx.x;
+        int64_t e = -1;
+        if (t < s.head) e = t;
+        else if (t >= 64 && t < 64 + kVec && s.head + s.nvec * kVec + (t - 64) < s.count)
+            e = s.head + s.nvec * kVec + (t - 64);
+        if (e >= 0) {
+            DescCursor c2;
+            c2.d = descs;
+            c2.n = n_descs;
+            c2.load(desc_at(descs, n_descs, e));
+            const int64_t j = c2.index(e);
+            if (j >= 0) c2.ptr[j] = flat[e];
+        }
     }
 }
 
@@ -858,8 +901,9 @@ int zero_flat_scatter(const void* flat, int64_t flat_count, const zero_tensor_de
     if (flat_count < 0 || n_descs < 0) return ZERO_EINVAL;
     if (flat_count == 0 || n_descs == 0) return ZERO_OK;
     if (!flat || !descs) return ZERO_EINVAL;
-    const int64_t blocks = (flat_count + kTile - 1) / kTile;
-    return launch(flat_scatter_kernel, blocks, stream, (const uint16_t*)flat, flat_count, descs,
+    const void* p = flat;
+    const Split s = split_for(vector_head(&p, 1, nullptr, 0), flat_count);
+    return launch(flat_scatter_kernel, tile_blocks(s), stream, (const uint16_t*)flat, s, descs,
                   n_descs);
 }
 
