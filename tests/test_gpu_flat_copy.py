@@ -115,3 +115,89 @@ def test_fragmented_group_into_buckets_and_back():
         assert np.array_equal(to_np16(tensors[k]), back[k])
     got = np.concatenate([to_np16(t) for t in tensors])
     assert np.array_equal(got, np.concatenate(back))
+
+
+
+LLAMA_PER_LAYER = 9          # q, k, v, o, gate, up, down, two norm gains
+
+
+def _layer_range(wl, offs, layer):
+    k0 = 1 + LLAMA_PER_LAYER * layer                 # tensor 0 is the embedding
+    k1 = k0 + LLAMA_PER_LAYER - 1
+    return k0, k1, int(offs[k0]), int(offs[k1] + wl.numels[k1])
+
+
+def _time_gather(out, descs, reps=5):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        Z.zero_flat_gather(out, descs)
+    ev[1].record()
+    ev[1].synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
+@pytest.mark.parametrize("ownership", ["flat_partition", "whole_tensor"])
+def test_zero3_layer_gather(ownership):
+    """Stage 3 keeps each parameter only with its owner and assembles a layer's
+    full 16-bit parameters just before the layer runs, dropping them after
+    (wmrh.cn ZeRO article, section 2.2.3; ZeRO 优化器, "ZeRO Stage 3").  On one
+    GPU the owners' stores are separate allocations and the assembly is
+    zero_flat_gather into one layer buffer:
+
+    * flat_partition: owner p holds [p*P, (p+1)*P) of the flat buffer (ZeRO-2
+      source walkthrough, section 2.1); a layer's range takes one descriptor per
+      overlapping partition piece, cutting through tensors;
+    * whole_tensor: tensor i belongs to owner i mod N, which keeps its tensors
+      packed back to back (ZeRO 优化器, "ZeRO Stage 3", inter-tensor split).
+
+    LLaMA-7B shapes, N = 8, bf16; layers 0 and 31 and two layers that straddle a
+    partition boundary (3 and 16).  The gathered layer must
+    equal the oracle's gather of the same pieces and the layer's parameters as
+    generated directly for that flat range."""
+    from synth import inputs as I
+    wl = W.WORKLOADS["llama7b"]
+    offs, parts, padded = oracle.layout(wl.numels, wl.world, wl.align)
+    n = wl.world
+    if ownership == "flat_partition":
+        stores = [I.device_param16(wl, offs, int(parts[p]), int(parts[p + 1])) for p in range(n)]
+    else:
+        # owner p packs tensors p, p+N, ... ; where[i] = (owner, offset in its store)
+        where, sizes = {}, [0] * n
+        for i, m in enumerate(wl.numels):
+            where[i] = (i % n, sizes[i % n])
+            sizes[i % n] += int(m)
+        stores = [torch.empty(sizes[p], dtype=torch.bfloat16, device="cuda") for p in range(n)]
+        for i, m in enumerate(wl.numels):
+            p, o = where[i]
+            I.device_param16(wl, offs, int(offs[i]), int(offs[i] + m), out=stores[p][o:o + int(m)])
+    biggest = max(_layer_range(wl, offs, 0)[3] - _layer_range(wl, offs, 0)[2], 1)
+    layer_buf = torch.empty(biggest, dtype=torch.bfloat16, device="cuda")
+    for layer in (0, 3, 16, 31):
+        k0, k1, a, b = _layer_range(wl, offs, layer)
+        pieces, poffs = [], []
+        if ownership == "flat_partition":
+            for p in range(n):
+                lo, hi = max(a, int(parts[p])), min(b, int(parts[p + 1]))
+                if lo < hi:
+                    pieces.append(stores[p][lo - int(parts[p]):hi - int(parts[p])])
+                    poffs.append(lo - a)
+        else:
+            for i in range(k0, k1 + 1):
+                p, o = where[i]
+                pieces.append(stores[p][o:o + int(wl.numels[i])])
+                poffs.append(int(offs[i]) - a)
+        if ownership == "flat_partition":
+            assert len(pieces) == (2 if layer in (3, 16) else 1)
+        descs = Z.tensor_descs(pieces, poffs)
+        out = layer_buf[:b - a]
+        out.fill_(float("nan"))
+        Z.zero_flat_gather(out, descs)
+        torch.cuda.synchronize()
+        got = to_np16(out)
+        want = oracle.flat_gather([to_np16(t) for t in pieces], poffs, b - a)
+        assert np.array_equal(got, want), (ownership, layer)
+        assert np.array_equal(got, I.host_param16(wl, offs, a, b, threads=8)), (ownership, layer)
+        ms = _time_gather(out, descs)
+        print(f"{ownership} layer {layer}: {b - a} elements from {len(pieces)} pieces, "
+              f"{ms:.3f} ms, {4 * (b - a) / ms / 1e6:.0f} GB/s", flush=True)
