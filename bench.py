@@ -33,7 +33,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "zero_partitioned_mixed_shard_amd", "csrc", "zero_shard.hip")
+# the sources the reduce and AdamW kernels are built from (the flat copy
+# kernels live in csrc/zero_flat.hip and do not affect their counters)
+KERNEL_SRCS = [os.path.join(ROOT, "zero_partitioned_mixed_shard_amd", "csrc", f)
+               for f in ("zero_common.h", "zero_shard.hip")]
 COUNTERS = {w: os.path.join(ROOT, "profiles", f"adamw_reduce_{w}_hbm_counters.md")
             for w in ("llama7b", "llama70b")}
 
@@ -45,7 +48,10 @@ def measured_traffic(kernel: str, workload: str):
     import hashlib
     import re
     try:
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+        h = hashlib.sha256()
+        for f in KERNEL_SRCS:
+            h.update(open(f, "rb").read())
+        src = h.hexdigest()[:16]
         text = open(COUNTERS[workload]).read()
     except (OSError, KeyError):
         return None

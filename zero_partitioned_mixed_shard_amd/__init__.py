@@ -1,10 +1,11 @@
 """Python binding of the ZeRO-1/2 owner-shard step library (libzero_shard.so).
 
 Argument marshalling only: every phase runs in the HIP kernels of
-``csrc/zero_shard.hip`` behind the C ABI of ``include/zero_shard.h``.  The
-functions keep the C names.  Device buffers are torch tensors (device memory
-and streams are all torch is used for); 16-bit data is passed as
-torch.float16 / torch.bfloat16 tensors, fp32 state as torch.float32.  There is no fallback: if the library is missing, importing
+``csrc/zero_shard.hip`` and ``csrc/zero_flat.hip`` behind the C ABI of
+``include/zero_shard.h``.  The functions keep the C names.  Device buffers are
+torch tensors (device memory and streams are all torch is used for); 16-bit
+data is passed as torch.float16 / torch.bfloat16 tensors, fp32 state as
+torch.float32.  There is no fallback: if the library is missing, importing
 this package raises.
 """
 from __future__ import annotations

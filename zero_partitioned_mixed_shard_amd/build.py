@@ -6,7 +6,9 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "zero_shard.hip")
+# owner-step kernels + C ABI, and the flat copy kernels; zero_common.h is
+# included by both
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("zero_shard.hip", "zero_flat.hip")]
 LIB = os.path.join(PKG, "libzero_shard.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -23,7 +25,7 @@ FLAGS = [
 
 def build(extra=()) -> str:
     tmp = LIB + ".tmp"
-    subprocess.run([HIPCC, *FLAGS, *extra, "-o", tmp, SRC], check=True)
+    subprocess.run([HIPCC, *FLAGS, *extra, "-o", tmp, *SRCS], check=True)
     os.replace(tmp, LIB)
     return LIB
 

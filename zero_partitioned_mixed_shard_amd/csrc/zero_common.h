@@ -1,0 +1,133 @@
+// zero_common.h -- internal to the library: tile geometry, 128-bit memory
+// helpers, pointer-alignment split and the typed launcher shared by the
+// owner-step kernels (zero_shard.hip) and the flat copy kernels
+// (zero_flat.hip).  Each translation unit gets its own internal copy.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+
+#include "zero_shard.h"
+
+namespace {
+
+constexpr int kThreads = 256;          // 4 wave64s per block
+constexpr int kVec = 8;                // elements per lane (one 128-bit 16-bit access)
+constexpr int kTile = kThreads * kVec; // elements per block
+constexpr int kFold = 2048;            // partials folded per block per fold pass
+constexpr int kMaxStreamBlocks = 256 * 8;  // grid-stride kernels off the hot path
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// How the elements of a call map onto tiles.  With `aligned`, lanes run the
+// 128-bit path over [head, head + 8*nvec) and block 0 also does the `head`
+// leading and the < 8 trailing elements one by one; otherwise every lane
+// walks its 8 elements with 16/32-bit accesses.
+struct Split {
+    int64_t head, nvec, count;
+    int aligned;
+};
+
+// ---------------------------------------------------------------- memory ----
+__device__ __forceinline__ u32x4 load_nt(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store_nt(uint16_t* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 load_b128(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store_b128(uint16_t* p, u32x4 v) {
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ f32x4 load_f4(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ void store_f4(float* p, f32x4 v) {
+    *reinterpret_cast<f32x4*>(p) = v;
+}
+__device__ __forceinline__ uint16_t half_of(u32x4 w, int k) {
+    return (uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu));
+}
+__device__ __forceinline__ u32x4 pack8(const uint16_t* h) {
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
+    return w;
+}
+__device__ __forceinline__ int64_t lane_tile() {
+    return (int64_t)blockIdx.x * kThreads + threadIdx.x;
+}
+
+// ------------------------------------------------------------ host -------
+inline bool valid_dtype(int32_t dt) { return dt == ZERO_FP16 || dt == ZERO_BF16; }
+
+// Leading elements to handle one by one so that every pointer is 16-byte
+// aligned for the vector body, or -1 when no such count exists.
+inline int64_t vector_head(const void* const* p16, int n16, const void* const* p32, int n32) {
+    int64_t head = -1;
+    for (int k = 0; k < n16; ++k) {
+        const uintptr_t a = (uintptr_t)p16[k];
+        if (a & 1) return -1;
+        const int64_t h = (int64_t)((16 - (a & 15)) & 15) / 2;
+        if (head < 0) head = h;
+        else if (head != h) return -1;
+    }
+    for (int k = 0; k < n32; ++k) {
+        const uintptr_t a = (uintptr_t)p32[k];
+        if (a & 3) return -1;
+        const int64_t h = (int64_t)((16 - (a & 15)) & 15) / 4;
+        if (head < 0) head = h;
+        else if ((head & 3) != h) return -1;
+    }
+    return head < 0 ? 0 : head;
+}
+
+inline Split split_for(int64_t head, int64_t count) {
+    Split s;
+    s.count = count;
+    if (head < 0) {
+        s.head = 0;
+        s.nvec = 0;
+        s.aligned = 0;
+        return s;
+    }
+    if (head > count) head = count;
+    s.head = head;
+    s.nvec = (count - head) / kVec;
+    s.aligned = 1;
+    return s;
+}
+
+// Blocks of a tile kernel: one per 256 lane-tiles, at least one.
+inline int64_t tile_blocks(const Split& s) {
+    const int64_t lanes = s.aligned ? s.nvec : (s.count + kVec - 1) / kVec;
+    const int64_t b = (lanes + kThreads - 1) / kThreads;
+    return b < 1 ? 1 : b;
+}
+
+// Upper bound of tile_blocks over all alignments of `count` elements.
+inline int64_t max_tile_blocks(int64_t count) {
+    return (count + kTile - 1) / kTile + 1;
+}
+
+// Launches `kernel` with its arguments converted to the kernel's parameter
+// types and returns this launch's own status (not a stale thread-local one).
+template <typename... KArgs, typename... Args>
+inline int launch(void (*kernel)(KArgs...), int64_t grid, hipStream_t stream, Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    if (grid < 1 || grid > 0x7FFFFFFF) return ZERO_ERANGE;
+    std::tuple<KArgs...> packed(static_cast<KArgs>(args)...);
+    void* ptrs[sizeof...(KArgs)];
+    int i = 0;
+    std::apply([&](auto&... a) { ((ptrs[i++] = (void*)&a), ...); }, packed);
+    const hipError_t err =
+        hipLaunchKernel((const void*)kernel, dim3((unsigned)grid), dim3(kThreads), ptrs, 0, stream);
+    return err == hipSuccess ? ZERO_OK : ZERO_EDEVICE;
+}
+
+}  // namespace

@@ -33,24 +33,11 @@
 //     -ffp-contract=off and with correctly rounded fp32 division and square
 //     root, so the result does not depend on instruction selection.
 
-#include <hip/hip_runtime.h>
 #include <math.h>
-#include <stdint.h>
 
-#include <tuple>
-
-#include "zero_shard.h"
+#include "zero_common.h"
 
 namespace {
-
-constexpr int kThreads = 256;          // 4 wave64s per block
-constexpr int kVec = 8;                // elements per lane (one 128-bit 16-bit access)
-constexpr int kTile = kThreads * kVec; // elements per block
-constexpr int kFold = 2048;            // partials folded per block per fold pass
-constexpr int kMaxStreamBlocks = 256 * 8;  // grid-stride kernels off the hot path
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct RankPtrs {
     const uint16_t* p[ZERO_MAX_RANKS];
@@ -59,47 +46,6 @@ struct RankPtrs {
 struct AdamConsts {
     float decay, b1, omb1, b2, omb2, bc1, bc2, lr, eps, max_norm;
 };
-
-// How the elements of a call map onto tiles.  With `aligned`, lanes run the
-// 128-bit path over [head, head + 8*nvec) and block 0 also does the `head`
-// leading and the < 8 trailing elements one by one; otherwise every lane
-// walks its 8 elements with 16/32-bit accesses.
-struct Split {
-    int64_t head, nvec, count;
-    int aligned;
-};
-
-// ---------------------------------------------------------------- memory ----
-__device__ __forceinline__ u32x4 load_nt(const uint16_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ void store_nt(uint16_t* p, u32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-}
-__device__ __forceinline__ u32x4 load_b128(const uint16_t* p) {
-    return *reinterpret_cast<const u32x4*>(p);
-}
-__device__ __forceinline__ void store_b128(uint16_t* p, u32x4 v) {
-    *reinterpret_cast<u32x4*>(p) = v;
-}
-__device__ __forceinline__ f32x4 load_f4(const float* p) {
-    return *reinterpret_cast<const f32x4*>(p);
-}
-__device__ __forceinline__ void store_f4(float* p, f32x4 v) {
-    *reinterpret_cast<f32x4*>(p) = v;
-}
-__device__ __forceinline__ uint16_t half_of(u32x4 w, int k) {
-    return (uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu));
-}
-__device__ __forceinline__ u32x4 pack8(const uint16_t* h) {
-    u32x4 w;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
-    return w;
-}
-__device__ __forceinline__ int64_t lane_tile() {
-    return (int64_t)blockIdx.x * kThreads + threadIdx.x;
-}
 
 // ------------------------------------------------------- 16-bit formats ----
 template <int DT>
@@ -343,192 +289,6 @@ finalize_kernel(const double* __restrict__ in_sum, const uint32_t* __restrict__ 
     }
 }
 
-// ------------------------------------------- flat <-> tensors (copy) -------
-// Last descriptor whose offset is <= e, or -1.
-__device__ __forceinline__ int64_t desc_at(const zero_tensor_desc* d, int64_t n, int64_t e) {
-    int64_t lo = 0, hi = n;                  // first index with offset > e
-    while (lo < hi) {
-        const int64_t mid = lo + (hi - lo) / 2;
-        if (d[mid].offset <= e) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo - 1;
-}
-
-// A lane's view of the descriptor table: the tensor holding the flat
-// elements it is at, advanced forward only.
-struct DescCursor {
-    const zero_tensor_desc* d;
-    int64_t n, k, off, numel, next;
-    uint16_t* ptr;
-
-    __device__ __forceinline__ void load(int64_t kk) {
-        k = kk;
-        ptr = nullptr;
-        off = 0;
-        numel = 0;
-        if (k >= 0) {
-            ptr = (uint16_t*)d[k].ptr;
-            off = d[k].offset;
-            numel = d[k].numel;
-        }
-        next = k + 1 < n ? d[k + 1].offset : INT64_MAX;
-    }
-    __device__ __forceinline__ void seek(int64_t e) {   // e never decreases
-        while (next <= e) load(k + 1);
-    }
-    // index of flat element e in the current tensor, or -1 if e is in a gap
-    __device__ __forceinline__ int64_t index(int64_t e) const {
-        const int64_t j = e - off;
-        return (k >= 0 && j >= 0 && j < numel) ? j : -1;
-    }
-};
-
-// 8 consecutive 16-bit values starting at a 2-byte aligned address, read as
-// the two aligned 16-byte chunks that hold them.  Both chunks lie in the
-// pages of the first and last value, so nothing outside them is touched.
-__device__ __forceinline__ u32x4 load8_unaligned(const uint16_t* p) {
-    const uintptr_t a = (uintptr_t)p;
-    const u32x4* c = (const u32x4*)(a & ~(uintptr_t)15);
-    const int sh = (int)((a & 15) >> 1);     // 0..7 elements into the first chunk
-    const u32x4 c0 = __builtin_nontemporal_load(c);
-    if (sh == 0) return c0;
-    const u32x4 c1 = __builtin_nontemporal_load(c + 1);
-    const uint32_t w[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-    u32x4 o;
-    switch (sh) {
-#define ZERO_EVEN(T) case 2 * T: o[0] = w[T]; o[1] = w[T + 1]; o[2] = w[T + 2]; o[3] = w[T + 3]; break;
-#define ZERO_ODD(T)                                            \
-    case 2 * T + 1:                                            \
-        o[0] = __builtin_amdgcn_alignbit(w[T + 1], w[T], 16);  \
-        o[1] = __builtin_amdgcn_alignbit(w[T + 2], w[T + 1], 16); \
-        o[2] = __builtin_amdgcn_alignbit(w[T + 3], w[T + 2], 16); \
-        o[3] = __builtin_amdgcn_alignbit(w[T + 4], w[T + 3], 16); \
-        break;
-        ZERO_ODD(0) ZERO_EVEN(1) ZERO_ODD(1) ZERO_EVEN(2) ZERO_ODD(2) ZERO_EVEN(3) ZERO_ODD(3)
-#undef ZERO_EVEN
-#undef ZERO_ODD
-        default: o = c0; break;
-    }
-    return o;
-}
-
-// Gather: one 8-element tile of the flat buffer per lane (aligned through
-// the head split); a tile inside one tensor takes the 128-bit path, others
-// go element by element.  Thread 0 finds the block's first tensor by binary
-// search; lanes walk forward from it.
-__global__ void __launch_bounds__(kThreads)
-flat_gather_kernel(uint16_t* __restrict__ flat, Split s, const zero_tensor_desc* __restrict__ descs,
-                   int64_t n_descs) {
-    __shared__ int64_t s_first;
-    const int64_t base = s.aligned ? s.head + (int64_t)blockIdx.x * kTile
-                                   : (int64_t)blockIdx.x * kTile;
-    if (threadIdx.x == 0) s_first = desc_at(descs, n_descs, blockIdx.x == 0 ? 0 : base);
-    __syncthreads();
-    DescCursor cur;
-    cur.d = descs;
-    cur.n = n_descs;
-    cur.load(s_first);
-    const int64_t i = lane_tile();
-    const int64_t e0 = s.aligned ? s.head + i * kVec : i * kVec;
-    const bool vec_lane = s.aligned && i < s.nvec;
-    if (vec_lane || (!s.aligned && e0 < s.count)) {
-        cur.seek(e0);
-        const int64_t j0 = cur.index(e0);
-        if (vec_lane && j0 >= 0 && j0 + kVec <= cur.numel) {
-            store_nt(flat + e0, load8_unaligned(cur.ptr + j0));
-        } else {
-            for (int64_t e = e0; e < e0 + kVec && e < s.count; ++e) {
-                cur.seek(e);
-                const int64_t j = cur.index(e);
-                flat[e] = j >= 0 ? cur.ptr[j] : (uint16_t)0;
-            }
-        }
-    }
-    if (s.aligned && blockIdx.x == 0) {      // head and tail, one element per lane
-        const int t = threadIdx.x;
-        int64_t e = -1;
-        if (t < s.head) e = t;
-        else if (t >= 64 && t < 64 + kVec && s.head + s.nvec * kVec + (t - 64) < s.count)
-            e = s.head + s.nvec * kVec + (t - 64);
-        if (e >= 0) {
-            DescCursor c2;
-            c2.d = descs;
-            c2.n = n_descs;
-            c2.load(desc_at(descs, n_descs, e));
-            const int64_t j = c2.index(e);
-            flat[e] = j >= 0 ? c2.ptr[j] : (uint16_t)0;
-        }
-    }
-}
-
-// 8 consecutive 16-bit values (packed in w) to a 2-byte aligned address:
-// one 16-byte store when the address is 4-byte aligned, else a 16-bit store,
-// a 12-byte store and a 16-bit store.  Only these 16 bytes are written.
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
-
-__device__ __forceinline__ void store8_unaligned(uint16_t* p, u32x4 w) {
-    if (((uintptr_t)p & 3) == 0) {
-        *reinterpret_cast<u32x4_a4*>(p) = w;
-        return;
-    }
-    p[0] = (uint16_t)(w[0] & 0xFFFFu);
-    u32x3_a4 mid;
-    mid[0] = __builtin_amdgcn_alignbit(w[1], w[0], 16);
-    mid[1] = __builtin_amdgcn_alignbit(w[2], w[1], 16);
-    mid[2] = __builtin_amdgcn_alignbit(w[3], w[2], 16);
-    *reinterpret_cast<u32x3_a4*>(p + 1) = mid;
-    p[7] = (uint16_t)(w[3] >> 16);
-}
-
-// Scatter: one 8-element tile of the flat buffer per lane (aligned through
-// the head split), the mirror of the gather.
-__global__ void __launch_bounds__(kThreads)
-flat_scatter_kernel(const uint16_t* __restrict__ flat, Split s,
-                    const zero_tensor_desc* __restrict__ descs, int64_t n_descs) {
-    __shared__ int64_t s_first;
-    const int64_t base = s.aligned ? s.head + (int64_t)blockIdx.x * kTile
-                                   : (int64_t)blockIdx.x * kTile;
-    if (threadIdx.x == 0) s_first = desc_at(descs, n_descs, blockIdx.x == 0 ? 0 : base);
-    __syncthreads();
-    DescCursor cur;
-    cur.d = descs;
-    cur.n = n_descs;
-    cur.load(s_first);
-    const int64_t i = lane_tile();
-    const int64_t e0 = s.aligned ? s.head + i * kVec : i * kVec;
-    const bool vec_lane = s.aligned && i < s.nvec;
-    if (vec_lane || (!s.aligned && e0 < s.count)) {
-        cur.seek(e0);
-        const int64_t j0 = cur.index(e0);
-        if (vec_lane && j0 >= 0 && j0 + kVec <= cur.numel) {
-            store8_unaligned(cur.ptr + j0, load_nt(flat + e0));
-        } else {
-            for (int64_t e = e0; e < e0 + kVec && e < s.count; ++e) {
-                cur.seek(e);
-                const int64_t j = cur.index(e);
-                if (j >= 0) cur.ptr[j] = flat[e];
-            }
-        }
-    }
-    if (s.aligned && blockIdx.x == 0) {      // head and tail, one element per lane
-        const int t = threadIdx.x;
-        int64_t e = -1;
-        if (t < s.head) e = t;
-        else if (t >= 64 && t < 64 + kVec && s.head + s.nvec * kVec + (t - 64) < s.count)
-            e = s.head + s.nvec * kVec + (t - 64);
-        if (e >= 0) {
-            DescCursor c2;
-            c2.d = descs;
-            c2.n = n_descs;
-            c2.load(desc_at(descs, n_descs, e));
-            const int64_t j = c2.index(e);
-            if (j >= 0) c2.ptr[j] = flat[e];
-        }
-    }
-}
-
 // ------------------------------------------------------------- AdamW -------
 struct AdamElem {
     float p, m, v;
@@ -617,57 +377,6 @@ adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restri
 }
 
 // --------------------------------------------------------------- host ------
-bool valid_dtype(int32_t dt) { return dt == ZERO_FP16 || dt == ZERO_BF16; }
-
-// Leading elements to handle one by one so that every pointer is 16-byte
-// aligned for the vector body, or -1 when no such count exists.
-int64_t vector_head(const void* const* p16, int n16, const void* const* p32, int n32) {
-    int64_t head = -1;
-    for (int k = 0; k < n16; ++k) {
-        const uintptr_t a = (uintptr_t)p16[k];
-        if (a & 1) return -1;
-        const int64_t h = (int64_t)((16 - (a & 15)) & 15) / 2;
-        if (head < 0) head = h;
-        else if (head != h) return -1;
-    }
-    for (int k = 0; k < n32; ++k) {
-        const uintptr_t a = (uintptr_t)p32[k];
-        if (a & 3) return -1;
-        const int64_t h = (int64_t)((16 - (a & 15)) & 15) / 4;
-        if (head < 0) head = h;
-        else if ((head & 3) != h) return -1;
-    }
-    return head < 0 ? 0 : head;
-}
-
-Split split_for(int64_t head, int64_t count) {
-    Split s;
-    s.count = count;
-    if (head < 0) {
-        s.head = 0;
-        s.nvec = 0;
-        s.aligned = 0;
-        return s;
-    }
-    if (head > count) head = count;
-    s.head = head;
-    s.nvec = (count - head) / kVec;
-    s.aligned = 1;
-    return s;
-}
-
-// Blocks of a tile kernel: one per 256 lane-tiles, at least one.
-int64_t tile_blocks(const Split& s) {
-    const int64_t lanes = s.aligned ? s.nvec : (s.count + kVec - 1) / kVec;
-    const int64_t b = (lanes + kThreads - 1) / kThreads;
-    return b < 1 ? 1 : b;
-}
-
-// Upper bound of tile_blocks over all alignments of `count` elements.
-int64_t max_tile_blocks(int64_t count) {
-    return (count + kTile - 1) / kTile + 1;
-}
-
 // Workspace layout: fold levels of (double sums, uint32 flags), each level
 // 8-byte aligned; level 0 has one partial per tile block.
 struct Levels {
@@ -701,21 +410,6 @@ unsigned stream_grid(int64_t items) {
     if (b < 1) b = 1;
     if (b > kMaxStreamBlocks) b = kMaxStreamBlocks;
     return (unsigned)b;
-}
-
-// Launches `kernel` with its arguments converted to the kernel's parameter
-// types and returns this launch's own status (not a stale thread-local one).
-template <typename... KArgs, typename... Args>
-int launch(void (*kernel)(KArgs...), int64_t grid, hipStream_t stream, Args... args) {
-    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
-    if (grid < 1 || grid > 0x7FFFFFFF) return ZERO_ERANGE;
-    std::tuple<KArgs...> packed(static_cast<KArgs>(args)...);
-    void* ptrs[sizeof...(KArgs)];
-    int i = 0;
-    std::apply([&](auto&... a) { ((ptrs[i++] = (void*)&a), ...); }, packed);
-    const hipError_t err =
-        hipLaunchKernel((const void*)kernel, dim3((unsigned)grid), dim3(kThreads), ptrs, 0, stream);
-    return err == hipSuccess ? ZERO_OK : ZERO_EDEVICE;
 }
 
 // Folds the level-0 partials into *res: fold passes, then the finalize block.
@@ -884,27 +578,6 @@ int zero_init_master(float* master, const void* param16, int64_t count, int32_t 
     const uint16_t* p = (const uint16_t*)param16;
     return dtype == ZERO_FP16 ? launch(init_master_kernel<ZERO_FP16>, grid, stream, master, p, count)
                               : launch(init_master_kernel<ZERO_BF16>, grid, stream, master, p, count);
-}
-
-int zero_flat_gather(void* flat, int64_t flat_count, const zero_tensor_desc* descs,
-                     int64_t n_descs, hipStream_t stream) {
-    if (flat_count < 0 || n_descs < 0) return ZERO_EINVAL;
-    if (flat_count == 0) return ZERO_OK;
-    if (!flat || (n_descs > 0 && !descs)) return ZERO_EINVAL;
-    const void* p = flat;
-    const Split s = split_for(vector_head(&p, 1, nullptr, 0), flat_count);
-    return launch(flat_gather_kernel, tile_blocks(s), stream, (uint16_t*)flat, s, descs, n_descs);
-}
-
-int zero_flat_scatter(const void* flat, int64_t flat_count, const zero_tensor_desc* descs,
-                      int64_t n_descs, hipStream_t stream) {
-    if (flat_count < 0 || n_descs < 0) return ZERO_EINVAL;
-    if (flat_count == 0 || n_descs == 0) return ZERO_OK;
-    if (!flat || !descs) return ZERO_EINVAL;
-    const void* p = flat;
-    const Split s = split_for(vector_head(&p, 1, nullptr, 0), flat_count);
-    return launch(flat_scatter_kernel, tile_blocks(s), stream, (const uint16_t*)flat, s, descs,
-                  n_descs);
 }
 
 int zero_reduce_owned(void* dst, const void* const* srcs, int32_t n_ranks, int64_t count,
