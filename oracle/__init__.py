@@ -165,14 +165,18 @@ def buckets(numels: Sequence[int], cap: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Bucket copy-in (gather into the flat buffer) and write-back (scatter out)
 # --------------------------------------------------------------------------
-def flat_gather(tensors: Sequence[np.ndarray], offsets: Sequence[int], flat_count: int) -> np.ndarray:
+def flat_gather(tensors: Sequence[np.ndarray], offsets: Sequence[int], flat_count: int,
+                out: np.ndarray | None = None) -> np.ndarray:
+    """Whole flat buffer (written into `out` when given): tensors at their
+    offsets, 0 everywhere else."""
     ts = [np.ascontiguousarray(t, dtype=np.uint16) for t in tensors]
     offs = np.ascontiguousarray(offsets, dtype=np.int64)
     numel = np.array([t.size for t in ts], dtype=np.int64)
     assert offs.size == len(ts)
     assert all(o >= 0 and o + n <= flat_count for o, n in zip(offs, numel))
     ptrs = (ctypes.c_void_p * max(1, len(ts)))(*[_p(t) for t in ts])
-    flat = np.empty(flat_count, dtype=np.uint16)
+    flat = np.empty(flat_count, dtype=np.uint16) if out is None else out
+    assert flat.dtype == np.uint16 and flat.size == flat_count and flat.flags.c_contiguous
     lib().oracle_flat_gather(_p(flat), flat_count, ptrs, _p(offs), _p(numel), len(ts))
     return flat
 

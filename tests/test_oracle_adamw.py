@@ -79,12 +79,16 @@ def test_first_step_closed_form(dtype):
     assert np.array_equal(st.param16, oracle.encode16(st.master, dtype))
 
 
-def test_matches_torch_adamw_step_by_step():
+@pytest.mark.parametrize("max_norm", [0.05, 1.0])
+def test_matches_torch_adamw_step_by_step(max_norm):
+    """torch.nn.utils.clip_grad_norm_ on the unscaled gradient, then
+    torch.optim.AdamW.  max_norm 0.05 clips every step (the norm is ~0.14),
+    1.0 never does."""
     n = 5000
     dtype = FP16
     hp = oracle.HParams(lr=float(np.float32(1e-3)), beta1=float(np.float32(0.9)),
                         beta2=float(np.float32(0.999)), eps=float(np.float32(1e-8)),
-                        weight_decay=float(np.float32(0.01)), max_grad_norm=1.0)
+                        weight_decay=float(np.float32(0.01)), max_grad_norm=max_norm)
     st = oracle.OwnerState.from_param16(_param16(n, dtype), dtype)
     scale = 2.0 ** 16
     worst = {"m": 0.0, "v": 0.0, "p": 0.0}
@@ -92,18 +96,20 @@ def test_matches_torch_adamw_step_by_step():
         red = oracle.reduce(_grads(n, 4, dtype, 1e-3, scale, step=t), dtype)
         inv = 1.0 / scale
         flag, sumsq = oracle.check(red, dtype, inv)
-        coef = oracle.clip_coef(hp.max_grad_norm, sumsq)
-        g = ((oracle.decode16(red, dtype).astype(np.float32) * np.float32(inv))
-             * np.float32(coef)).astype(np.float32)
+        g_unscaled = (oracle.decode16(red, dtype).astype(np.float32)
+                      * np.float32(inv)).astype(np.float32)
 
         p = torch.nn.Parameter(torch.from_numpy(st.master.copy()))
+        p.grad = torch.from_numpy(g_unscaled.copy())
+        norm = float(torch.nn.utils.clip_grad_norm_([p], max_norm))
+        assert (norm > max_norm) == (max_norm < 1.0)
+        g = p.grad.numpy().copy()
         opt = torch.optim.AdamW([p], lr=hp.lr, betas=(hp.beta1, hp.beta2), eps=hp.eps,
                                 weight_decay=hp.weight_decay, foreach=False, fused=False)
         # give torch the oracle's state as of step t-1
         opt.state[p]["step"] = torch.tensor(float(t - 1))
         opt.state[p]["exp_avg"] = torch.from_numpy(st.exp_avg.copy())
         opt.state[p]["exp_avg_sq"] = torch.from_numpy(st.exp_avg_sq.copy())
-        p.grad = torch.from_numpy(g)
         m_prev, v_prev, p_prev = st.exp_avg.copy(), st.exp_avg_sq.copy(), st.master.copy()
         opt.step()
         oracle.adamw(st.master, st.exp_avg, st.exp_avg_sq, st.param16, red, dtype, inv, sumsq,
@@ -115,11 +121,19 @@ def test_matches_torch_adamw_step_by_step():
         dm = np.abs(st.exp_avg - opt.state[p]["exp_avg"].numpy()) / (mag_m + 1e-30)
         dv = np.abs(st.exp_avg_sq - opt.state[p]["exp_avg_sq"].numpy()) / (mag_v + 1e-30)
         upd = np.abs(p_prev.astype(np.float64) - st.master)
-        dp = np.abs(st.master - p.detach().numpy()) / (_ulp32(st.master) + 8 * EPS32 * upd)
+        # torch's fp32 clip coefficient differs from the oracle's by a few ulp;
+        # through m that moves the update by lr*(1-b1)|g|*delta/bc1/(sqrt(vh)+eps)
+        delta = 0.0 if max_norm >= 1.0 else 8 * EPS32
+        bc1, bc2 = 1 - hp.beta1 ** t, 1 - hp.beta2 ** t
+        via_m = (hp.lr * (1 - hp.beta1) * np.abs(gd) * delta / bc1
+                 / (np.sqrt(st.exp_avg_sq / bc2) + hp.eps))
+        dp = np.abs(st.master - p.detach().numpy()) / (_ulp32(st.master) + 8 * EPS32 * upd + via_m)
         worst = {"m": max(worst["m"], dm.max()), "v": max(worst["v"], dv.max()),
                  "p": max(worst["p"], dp.max())}
-    assert worst["m"] <= 4 * EPS32
-    assert worst["v"] <= 4 * EPS32
+    # clipping adds torch's fp32 norm and coefficient (a few ulp) to both sides' terms
+    tol = 4 * EPS32 if max_norm >= 1.0 else 12 * EPS32
+    assert worst["m"] <= tol
+    assert worst["v"] <= 2 * tol
     assert worst["p"] <= 2.0
 
 
@@ -170,6 +184,16 @@ def test_skip_on_overflow_leaves_state_untouched():
     before = st.copy()
     grads = _grads(n, 8, dtype, 1e-3, scaler.scale, step=4)
     grads[3][1234] = synth.POS_INF[FP16]
+    # the AdamW phase on its own writes nothing when handed the flag
+    red = oracle.reduce(grads, dtype)
+    flag, sumsq = oracle.check(red, dtype, 1.0 / scaler.scale)
+    assert flag == 1
+    oracle.adamw(st.master, st.exp_avg, st.exp_avg_sq, st.param16, red, dtype,
+                 1.0 / scaler.scale, sumsq, flag, hp, t + 1)
+    for a, b in ((st.master, before.master), (st.exp_avg, before.exp_avg),
+                 (st.exp_avg_sq, before.exp_avg_sq), (st.param16, before.param16)):
+        assert np.array_equal(a.view(np.uint32 if a.dtype == np.float32 else np.uint16),
+                              b.view(np.uint32 if b.dtype == np.float32 else np.uint16))
     res, t2 = oracle.step([st], [grads], dtype, hp, scaler, t)
     assert res.overflow == 1 and not res.applied and t2 == t
     for a, b in ((st.master, before.master), (st.exp_avg, before.exp_avg),
@@ -205,6 +229,27 @@ def test_scale_invariance():
         assert np.array_equal(finals[0].exp_avg_sq.view(np.uint32),
                               other.exp_avg_sq.view(np.uint32))
         assert np.array_equal(finals[0].param16, other.param16)
+
+
+def test_divisor_averages_the_gradient():
+    """Averaging over N ranks is the sum divided by N, folded into the
+    unscale factor 1/(S*N): for N = 8 (a power of two, so every scaling is
+    exact) the squared norm is the summed one / 64, and the update equals the
+    one from the summed gradient at loss scale 8*S, bit for bit."""
+    n = 3000
+    dtype = FP16
+    hp = oracle.HParams(max_grad_norm=0.05)
+    a = oracle.OwnerState.from_param16(_param16(n, dtype), dtype)
+    b = a.copy()
+    plain = a.copy()
+    grads = _grads(n, 8, dtype, 1e-3, 1024.0)
+    ra, _ = oracle.step([a], [grads], dtype, hp, oracle.Scaler(1024.0), 0, divisor=8)
+    rb, _ = oracle.step([b], [grads], dtype, hp, oracle.Scaler(8 * 1024.0), 0)
+    rp, _ = oracle.step([plain], [grads], dtype, hp, oracle.Scaler(1024.0), 0)
+    assert ra.sumsq == rp.sumsq / 64 and ra.sumsq == rb.sumsq
+    for x, y in ((a.master, b.master), (a.exp_avg, b.exp_avg), (a.exp_avg_sq, b.exp_avg_sq)):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert not np.array_equal(a.exp_avg.view(np.uint32), plain.exp_avg.view(np.uint32))
 
 
 @pytest.mark.parametrize("world,clip", [(2, 0.0), (3, 1.0), (8, 0.5)])

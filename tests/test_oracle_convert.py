@@ -60,12 +60,15 @@ def test_encode_from_f32_structured(dtype):
     rng = np.random.default_rng(3)
     lows = np.array([0, 1, tie - 1, tie, tie + 1, (1 << low_bits) - 1,
                      *rng.integers(0, 1 << low_bits, 10)], dtype=np.uint64)
-    highs = np.arange(1 << (32 - low_bits), dtype=np.uint64) << np.uint64(low_bits)
-    pats = (highs[:, None] | lows[None, :]).ravel()
-    pats = np.concatenate([pats, rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64)])
-    x = pats.astype(np.uint32).view(np.float32)
-    got = oracle.encode16(x, dtype)
-    assert _same16(got, _library_cast(x, dtype), dtype).all()
+    n_high = 1 << (32 - low_bits)
+    step = 1 << 16                       # prefixes per chunk: small, reused buffers
+    for h0 in range(0, n_high, step):
+        highs = np.arange(h0, h0 + step, dtype=np.uint32) << np.uint32(low_bits)
+        x = (highs[:, None] | lows.astype(np.uint32)[None, :]).ravel().view(np.float32)
+        assert _same16(oracle.encode16(x, dtype), _library_cast(x, dtype), dtype).all(), h0
+    for k in range(4):
+        x = rng.integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        assert _same16(oracle.encode16(x, dtype), _library_cast(x, dtype), dtype).all()
 
 
 @pytest.mark.slow

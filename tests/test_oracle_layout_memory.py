@@ -5,6 +5,11 @@
   must be equal, contiguous, cover the padded buffer exactly once and the real
   elements [0, Phi) exactly once (ZeRO-2 source walkthrough, sections 2.1 and
   4.1: flatten, align, split into as many near-equal partitions as ranks).
+* Bucket copy-in / write-back (ZeRO-2 source walkthrough, sections 2.4, 4.2
+  and 4.4): a worked example by hand, then invariants on random tables --
+  write-back of a copy-in returns every tensor, elements no tensor covers
+  are 0 even in a buffer that held other bits, and the copy-in of the
+  write-back of a buffer keeps exactly the covered elements.
 * The pages' memory formulas and worked examples (tests/golden/pages_values.json).
 """
 import json
@@ -125,6 +130,43 @@ def test_buckets_brute_force():
     first = oracle.buckets(b.numels, cap)
     fills = [int(b.numels[first[k]:first[k + 1]].sum()) for k in range(first.size - 1)]
     assert len(fills) == 3 and max(fills) <= cap
+
+
+# ------------------------------------------------------ copy-in / write-back
+def test_flat_copy_worked_example():
+    # tensors [1 2 3] at offset 1 and [4] at offset 5 of a 7-element buffer
+    t0 = np.array([1, 2, 3], np.uint16)
+    t1 = np.array([4], np.uint16)
+    poisoned = np.full(7, 0xFFFF, np.uint16)
+    flat = oracle.flat_gather([t0, t1], [1, 5], 7, out=poisoned)
+    assert flat.tolist() == [0, 1, 2, 3, 0, 4, 0]
+    back = oracle.flat_scatter(np.array([9, 8, 7, 6, 5, 4, 3], np.uint16), [1, 5], [3, 1])
+    assert [b.tolist() for b in back] == [[8, 7, 6], [4]]
+    assert oracle.flat_gather([], [], 3, out=np.full(3, 7, np.uint16)).tolist() == [0, 0, 0]
+
+
+def test_flat_copy_invariants():
+    rng = np.random.default_rng(17)
+    for trial in range(200):
+        n = int(rng.integers(0, 9))
+        sizes = rng.integers(0, 13, n)
+        offs, cur = [], int(rng.integers(0, 4))
+        for m in sizes:                                   # sorted, gaps of 0..3
+            offs.append(cur)
+            cur += int(m) + int(rng.integers(0, 4))
+        count = cur + int(rng.integers(0, 4))
+        ts = [rng.integers(1, 65536, int(m)).astype(np.uint16) for m in sizes]
+        covered = np.zeros(count, bool)
+        for o, m in zip(offs, sizes):
+            covered[o:o + m] = True
+        flat = oracle.flat_gather(ts, offs, count,
+                                  out=rng.integers(1, 65536, count).astype(np.uint16))
+        assert (flat[~covered] == 0).all()
+        for t, b in zip(ts, oracle.flat_scatter(flat, offs, sizes)):
+            assert np.array_equal(t, b)
+        src = rng.integers(0, 65536, count).astype(np.uint16)
+        again = oracle.flat_gather(oracle.flat_scatter(src, offs, sizes), offs, count)
+        assert np.array_equal(again, np.where(covered, src, 0))
 
 
 # ---------------------------------------------------------------- memory
