@@ -66,7 +66,8 @@ enum zero_dtype {
  * zero_unscale_check_norm, read by zero_adamw_step on the device, and copied
  * to the host by the caller only for the loss-scale update.  16 bytes. */
 typedef struct zero_step_result {
-    double sumsq;        /* sum over the checked elements of (value * inv_scale)^2, fp64 */
+    double sumsq;        /* sum over the checked elements of (value * inv_scale)^2, fp64;
+                            value * inv_scale is the fp32 product                       */
     uint32_t overflow;   /* 1 if some checked element is +-inf or NaN, else 0          */
     float inv_scale;     /* the unscale factor the check used                           */
 } zero_step_result;
@@ -184,11 +185,12 @@ int zero_flat_gather(void* flat, int64_t flat_count, const zero_tensor_desc* des
 int zero_flat_scatter(const void* flat, int64_t flat_count, const zero_tensor_desc* descs,
                       int64_t n_descs, hipStream_t stream);
 
-/* Reduce to the owner: dst[i] = round16(g_0[i] + g_1[i] + ... + g_{N-1}[i]),
- * the additions done in fp64 in rank order and the result rounded once to
- * the 16-bit type, ties to even (exact for binary16: every fp64 partial sum
- * of at most 16 binary16 values is exact).  An inf/NaN input or a sum beyond
- * the 16-bit range gives inf/NaN in dst, which the check phase then flags.
+/* Reduce to the owner: dst[i] = round16(((0 + g_0[i]) + g_1[i]) + ... + g_{N-1}[i]),
+ * the additions done in fp32 (each rounded to nearest-even) in rank order
+ * starting from +0, and the result rounded once to the 16-bit type, ties to
+ * even.  Starting from +0 makes a column of -0 values sum to +0.  An inf/NaN
+ * input or a sum beyond the 16-bit range gives inf/NaN in dst, which the
+ * check phase then flags.
  * (ZeRO 优化器 "ZeRO Stage 1": after the reduce the owner holds the sum of all
  * ranks' gradients; ZeRO-2 source walkthrough section 三: the reduced data is
  * fp16/bf16.)
@@ -219,10 +221,10 @@ size_t zero_check_workspace_bytes(int64_t count);
 
 /* Unscale + overflow check + squared norm over grad16[0, count):
  *   overflow = some element is +-inf or NaN (exponent field all ones);
- *   sumsq    = sum of ((double)value * inv_scale)^2, accumulated in fp64
- *              (each square is exact; the summation order is fixed for a
- *              given count and pointer alignment, so repeated calls give
- *              identical bits).
+ *   sumsq    = sum of ((double)(value * inv_scale))^2, the product taken in
+ *              fp32 and the squares accumulated in fp64 (each square is
+ *              exact; the summation order is fixed for a given count and
+ *              pointer alignment, so repeated calls give identical bits).
  * With accumulate == 0 the call overwrites *res; with accumulate != 0 it adds
  * its sumsq to res->sumsq and ORs its flag into res->overflow, so several
  * owner ranges checked in turn on one stream form one global result.

@@ -88,7 +88,7 @@ def lib():
         L.oracle_buckets.argtypes = [P, i64, i64, P, P]
         L.oracle_buckets.restype = ctypes.c_int
         L.oracle_reduce.argtypes = [P, P, i32, i64, i32]
-        L.oracle_check.argtypes = [P, i64, i32, f64, P, P]
+        L.oracle_check.argtypes = [P, i64, i32, f32, P, P]
         L.oracle_clip_coef.argtypes = [f32, f64]
         L.oracle_clip_coef.restype = f32
         L.oracle_adam_consts_for.argtypes = [P, P]
@@ -224,7 +224,8 @@ def reduce(srcs: Sequence[np.ndarray], dtype: int, out: np.ndarray | None = None
 
 
 def check(red: np.ndarray, dtype: int, inv_scale: float, overflow: int = 0, sumsq: float = 0.0):
-    """-> (overflow, sumsq), accumulated onto the given starting values."""
+    """-> (overflow, sumsq), accumulated onto the given starting values.
+    inv_scale is taken as an fp32 value."""
     red = np.ascontiguousarray(red, dtype=np.uint16)
     fl = np.array([overflow], dtype=np.uint32)
     ss = np.array([sumsq], dtype=np.float64)
@@ -338,7 +339,7 @@ def step(owners: Sequence[OwnerState], grads: Sequence[Sequence[np.ndarray]], dt
     over the given owners, as the owners would agree on them before the
     update.  An overflow skips the update and leaves t unchanged.
     """
-    inv = 1.0 / (scaler.scale * divisor)
+    inv = float(np.float32(1.0 / (scaler.scale * divisor)))   # fp32(1/(S*D))
     reduced = [reduce(g, dtype) for g in grads]
     overflow, sumsq = 0, 0.0
     for red in reduced:

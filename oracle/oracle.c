@@ -27,8 +27,10 @@
  * ZeRO 优化器 "训练状态的冗余分析").  The optimizer runs on the fp32 partition, so
  * its per-element arithmetic is fp32, one IEEE rounding per operation, no fused
  * multiply-add (build with -ffp-contract=off).  Everything the pages leave open
- * is done in fp64: the gradient sum (exact for binary16 inputs), the norm, and
- * the scalar constants, each rounded once to its storage type.
+ * is read as follows: the gradient sum is taken in fp32, in rank order from +0,
+ * and rounded once to 16 bits; the unscaled gradient is the fp32 product of the
+ * value and 1/(S*D); the norm and the scalar constants are computed in fp64,
+ * each rounded once to its storage type.
  */
 #include <math.h>
 #include <stdint.h>
@@ -226,27 +228,31 @@ void oracle_flat_scatter(const uint16_t* flat, uint16_t* const* tensors, const i
 /* the 16-bit communication type.  ZeRO 优化器, "ZeRO Stage 1": after the      */
 /* reduce the owner holds the sum of every rank's gradient.  ZeRO-2 source     */
 /* walkthrough section 三: with reduce-scatter the communicated type is        */
-/* fp16/bf16.  The sum is taken in fp64 in rank order (exact for binary16).    */
+/* fp16/bf16.  The pages leave the accumulation open; it is read as fp32       */
+/* additions in rank order starting from +0, each rounded to nearest-even,    */
+/* then one rounding of the fp32 sum to the 16-bit type.  Every 16-bit value  */
+/* is exactly a float, so each addend enters unchanged.                        */
 /* ------------------------------------------------------------------------- */
 void oracle_reduce(uint16_t* red, const uint16_t* const* src, int32_t n_ranks,
                    int64_t count, int32_t dtype) {
     const double* val = value_table(dtype);
     fmt16 f = fmt_of(dtype);
     for (int64_t i = 0; i < count; ++i) {
-        double acc = val[src[0][i]];
-        for (int32_t r = 1; r < n_ranks; ++r) acc = acc + val[src[r][i]];
-        red[i] = encode16(acc, f);
+        float acc = 0.0f;
+        for (int32_t r = 0; r < n_ranks; ++r) acc = acc + (float)val[src[r][i]];
+        red[i] = encode16((double)acc, f);
     }
 }
 
 /* ------------------------------------------------------------------------- */
 /* Check: overflow = some element of the reduced slice is inf or NaN;         */
-/* sumsq = sum of (value * inv_scale)^2 in fp64 (each square is exact).       */
+/* sumsq = sum of g^2 in fp64, g = value * inv_scale as an fp32 product (each */
+/* square is exact in fp64).                                                  */
 /* wmrh.cn article section 3.1: fp16 training with dynamic loss scaling;      */
 /* section 3.3: gradient_clipping.  Results are accumulated into *overflow    */
 /* and *sumsq so several owner ranges can form one global result.             */
 /* ------------------------------------------------------------------------- */
-void oracle_check(const uint16_t* red, int64_t count, int32_t dtype, double inv_scale,
+void oracle_check(const uint16_t* red, int64_t count, int32_t dtype, float inv_scale,
                   uint32_t* overflow, double* sumsq) {
     const double* val = value_table(dtype);
     uint32_t flag = *overflow;
@@ -254,7 +260,7 @@ void oracle_check(const uint16_t* red, int64_t count, int32_t dtype, double inv_
     for (int64_t i = 0; i < count; ++i) {
         double x = val[red[i]];
         if (!isfinite(x)) flag = 1;
-        double g = x * inv_scale;
+        double g = (double)((float)x * inv_scale);
         s = s + g * g;
     }
     *overflow = flag;

@@ -9,8 +9,8 @@ skip path and accumulation over several owner ranges.
 
 Tolerances: reduced gradients, overflow flags and skip decisions bit-exact;
 fp32 master / m / v bit-equal or within 2e-6 relative; 16-bit copy within 1 ulp;
-sumsq within 1e-12 relative here (fp64 sums of exact squares; only the
-summation order differs).
+sumsq within 1e-12 relative here (fp64 sums of the exact squares of the fp32
+unscaled values; only the summation order differs).
 """
 import ctypes
 
@@ -131,6 +131,24 @@ def test_reduce_overflow_specials():
     Z.zero_reduce_owned(dst, [_dev16(h, FP16) for h in host])
     torch.cuda.synchronize()
     assert_bits16_equal(to_np16(dst), oracle.reduce(host, FP16), FP16)
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_reduce_fp32_accumulation_columns(dtype):
+    # columns where fp32 accumulation from +0 and an exact sum round differently
+    # (binary16 [2048, 1, 2^-14] -> 2048; bfloat16 [1, 2^-8, 2^-32] -> 1), the
+    # same addends in another order, and -0 columns (the sum starts from +0)
+    cols = {FP16: [(0x6800, 0x3C00, 0x0400), (0x0400, 0x3C00, 0x6800), (0x8000, 0x8000, 0x8000)],
+            BF16: [(0x3F80, 0x3B80, 0x2F80), (0x2F80, 0x3F80, 0x3B80), (0x8000, 0x8000, 0x8000)]}
+    want_hand = {FP16: [0x6800, 0x6800, 0x0000], BF16: [0x3F80, 0x3F80, 0x0000]}
+    reps = 4099                                  # vector path plus a ragged tail
+    host = [np.tile(np.array([c[r] for c in cols[dtype]], np.uint16), reps) for r in range(3)]
+    want = oracle.reduce(host, dtype)
+    assert want[:3].tolist() == want_hand[dtype]
+    dst = _dev16(np.zeros(host[0].size, np.uint16), dtype)
+    Z.zero_reduce_owned(dst, [_dev16(h, dtype) for h in host])
+    torch.cuda.synchronize()
+    assert_bits16_equal(to_np16(dst), want, dtype, "fp32 accumulation columns")
 
 
 # -------------------------------------------------------------- check ------

@@ -46,11 +46,16 @@ MUTANTS = {
     "gather_no_zero_fill": (C, "for (int64_t i = 0; i < flat_count; ++i) flat[i] = 0;", ""),
     "scatter_off_by_one": (C, "tensors[k][j] = flat[offset[k] + j];", "tensors[k][j] = flat[offset[k] + j + (j + 1 < numel[k])];"),
     # reduce and check
-    "reduce_drops_rank0": (C, "double acc = val[src[0][i]];", "double acc = 0.0;"),
-    "reduce_drops_last_rank": (C, "r < n_ranks; ++r) acc = acc + val", "r < n_ranks - 1; ++r) acc = acc + val"),
-    "reduce_accumulates_in_fp32": (C, "acc = acc + val[src[r][i]];", "acc = (double)(float)(acc + val[src[r][i]]);"),
+    "reduce_drops_rank0": (C, "for (int32_t r = 0; r < n_ranks; ++r) acc = acc + (float)val",
+                           "for (int32_t r = 1; r < n_ranks; ++r) acc = acc + (float)val"),
+    "reduce_drops_last_rank": (C, "r < n_ranks; ++r) acc = acc + (float)val", "r < n_ranks - 1; ++r) acc = acc + (float)val"),
+    "reduce_accumulates_in_fp64": (C, "float acc = 0.0f;\n        for (int32_t r = 0; r < n_ranks; ++r) acc = acc + (float)val[src[r][i]];",
+                                   "double acc = 0.0;\n        for (int32_t r = 0; r < n_ranks; ++r) acc = acc + val[src[r][i]];"),
+    "reduce_starts_from_rank0": (C, "float acc = 0.0f;\n        for (int32_t r = 0; r < n_ranks;",
+                                 "float acc = (float)val[src[0][i]];\n        for (int32_t r = 1; r < n_ranks;"),
     "check_misses_nan": (C, "if (!isfinite(x)) flag = 1;", "if (isinf(x)) flag = 1;"),
-    "check_norm_not_unscaled": (C, "double g = x * inv_scale;", "double g = x;"),
+    "check_norm_not_unscaled": (C, "double g = (double)((float)x * inv_scale);", "double g = x;"),
+    "check_unscale_in_fp64": (C, "double g = (double)((float)x * inv_scale);", "double g = x * (double)inv_scale;"),
     "check_l1_not_l2": (C, "s = s + g * g;", "s = s + fabs(g);"),
     "check_not_accumulated": (C, "uint32_t flag = *overflow;\n    double s = *sumsq;", "uint32_t flag = 0;\n    double s = 0.0;"),
     "clip_without_eps": (C, "(sqrt(sumsq) + 1e-6)", "(sqrt(sumsq))"),
@@ -82,7 +87,8 @@ MUTANTS = {
     "step_counts_skipped_steps": (PY, "    applied = not overflow\n    if applied:\n        t = t + 1\n",
                                   "    applied = not overflow\n    t = t + 1\n    if applied:\n"),
     "step_norm_per_owner": (PY, "overflow, sumsq = check(red, dtype, inv, overflow, sumsq)", "overflow, sumsq = check(red, dtype, inv)"),
-    "step_divisor_ignored": (PY, "inv = 1.0 / (scaler.scale * divisor)", "inv = 1.0 / scaler.scale"),
+    "step_divisor_ignored": (PY, "inv = float(np.float32(1.0 / (scaler.scale * divisor)))",
+                             "inv = float(np.float32(1.0 / scaler.scale))"),
     "step_scaler_not_updated": (PY, "    scaler.update(overflow)\n    return res, t", "    return res, t"),
 }
 

@@ -23,12 +23,11 @@
 // No MFMA: nothing here is a dense contraction.
 //
 // Numerics (the header gives the per-element definitions):
-//   * reduce: fp64 additions in rank order, then one rounding to 16 bits.  The
-//     fp64 -> 16-bit rounding is done as fp64 -> fp32 rounded to odd, then
-//     fp32 -> 16 bits to nearest-even; an intermediate format with at least
-//     two more significand bits, rounded to odd, makes the second rounding
-//     equal to a direct one (Boldo and Melquiond, "When double rounding is
-//     odd", 2005).
+//   * reduce: fp32 additions in rank order starting from +0, then one rounding
+//     to 16 bits, nearest-even (hardware convert for binary16, integer
+//     rounding of the upper half for bfloat16);
+//   * check: the unscaled value is the fp32 product float(v) * inv_scale; its
+//     square is exact in fp64 and summed in fp64;
 //   * AdamW: fp32 with one rounding per operation; the library is built with
 //     -ffp-contract=off and with correctly rounded fp32 division and square
 //     root, so the result does not depend on instruction selection.
@@ -82,24 +81,6 @@ __device__ __forceinline__ uint16_t from_f32<ZERO_BF16>(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// fp64 -> fp32 rounded to odd: truncate toward zero, and set the last bit if
-// anything was dropped.  Infinities and NaN pass through.
-__device__ __forceinline__ float f64_to_f32_odd(double d) {
-    float t = (float)d;                          // nearest-even
-    double back = (double)t;
-    if (back != d && __builtin_isfinite(t)) {
-        uint32_t u = __float_as_uint(t);
-        if (fabs(back) > fabs(d)) u -= 1u;       // was rounded away from zero
-        t = __uint_as_float(u | 1u);
-    }
-    return t;
-}
-
-template <int DT>
-__device__ __forceinline__ uint16_t round16(double d) {
-    return from_f32<DT>(f64_to_f32_odd(d));
-}
-
 // --------------------------------------------------- block reductions -----
 // Sum of `s` and OR of `f` over the block, in a fixed order; valid in thread 0.
 __device__ __forceinline__ void block_sum_or(double& s, uint32_t& f) {
@@ -124,11 +105,12 @@ __device__ __forceinline__ void block_sum_or(double& s, uint32_t& f) {
     }
 }
 
-// Accumulates one checked 16-bit value into (sq, bad).
+// Accumulates one checked 16-bit value into (sq, bad): the unscaled value is
+// the fp32 product float(b) * inv; its square is exact in fp64.
 template <int DT>
-__device__ __forceinline__ void check_acc(uint16_t b, double inv, double& sq, uint32_t& bad) {
+__device__ __forceinline__ void check_acc(uint16_t b, float inv, double& sq, uint32_t& bad) {
     bad |= nonfinite16<DT>(b) ? 1u : 0u;
-    const double x = (double)to_f32<DT>(b) * inv;   // exact
+    const double x = (double)(to_f32<DT>(b) * inv);
     sq = fma(x, x, sq);                             // x*x is exact in fp64
 }
 
@@ -143,9 +125,9 @@ init_master_kernel(float* __restrict__ master, const uint16_t* __restrict__ p16,
 // ------------------------------------------------------------ reduce -------
 template <int DT>
 __device__ __forceinline__ uint16_t reduce_one(const RankPtrs& src, int n_ranks, int64_t e) {
-    double acc = (double)to_f32<DT>(src.p[0][e]);
-    for (int r = 1; r < n_ranks; ++r) acc = acc + (double)to_f32<DT>(src.p[r][e]);
-    return round16<DT>(acc);
+    float acc = 0.0f;
+    for (int r = 0; r < n_ranks; ++r) acc = acc + to_f32<DT>(src.p[r][e]);
+    return from_f32<DT>(acc);
 }
 
 // Reduce of NR ranks; with CHECK also the overflow flag and squared norm of
@@ -154,7 +136,7 @@ __device__ __forceinline__ uint16_t reduce_one(const RankPtrs& src, int n_ranks,
 // same lane).
 template <int DT, int NR, bool CHECK>
 __global__ void __launch_bounds__(kThreads)
-reduce_kernel(uint16_t* dst, RankPtrs src, Split s, double inv, double* part_sum,
+reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, double* part_sum,
               uint32_t* part_flag) {
     double sq = 0.0;
     uint32_t bad = 0;
@@ -165,19 +147,20 @@ reduce_kernel(uint16_t* dst, RankPtrs src, Split s, double inv, double* part_sum
             u32x4 w[NR];
 #pragma unroll
             for (int r = 0; r < NR; ++r) w[r] = load_nt(src.p[r] + e);
-            double acc[kVec];
+            // fp32 additions in rank order from +0 (0 + -0 is +0, so the first
+            // addition is kept), one rounding to 16 bits
+            float acc[kVec];
 #pragma unroll
-            for (int k = 0; k < kVec; ++k) acc[k] = (double)to_f32<DT>(half_of(w[0], k));
+            for (int k = 0; k < kVec; ++k) acc[k] = 0.0f + to_f32<DT>(half_of(w[0], k));
 #pragma unroll
             for (int r = 1; r < NR; ++r) {
 #pragma unroll
-                for (int k = 0; k < kVec; ++k)
-                    acc[k] = acc[k] + (double)to_f32<DT>(half_of(w[r], k));
+                for (int k = 0; k < kVec; ++k) acc[k] = acc[k] + to_f32<DT>(half_of(w[r], k));
             }
             uint16_t h[kVec];
 #pragma unroll
             for (int k = 0; k < kVec; ++k) {
-                h[k] = round16<DT>(acc[k]);
+                h[k] = from_f32<DT>(acc[k]);
                 if (CHECK) check_acc<DT>(h[k], inv, sq, bad);
             }
             store_nt(dst + e, pack8(h));
@@ -213,7 +196,7 @@ reduce_kernel(uint16_t* dst, RankPtrs src, Split s, double inv, double* part_sum
 // ------------------------------------------------------------- check -------
 template <int DT>
 __global__ void __launch_bounds__(kThreads)
-check_kernel(const uint16_t* __restrict__ g, Split s, double inv, double* __restrict__ part_sum,
+check_kernel(const uint16_t* __restrict__ g, Split s, float inv, double* __restrict__ part_sum,
              uint32_t* __restrict__ part_flag) {
     double sq = 0.0;
     uint32_t bad = 0;
@@ -428,7 +411,7 @@ int fold_into(char* ws, const Levels& L, float inv_scale, int32_t accumulate, ze
 }
 
 template <int DT, bool CHECK>
-int launch_reduce_n(uint16_t* dst, const RankPtrs& src, int n, const Split& s, double inv,
+int launch_reduce_n(uint16_t* dst, const RankPtrs& src, int n, const Split& s, float inv,
                     double* ps, uint32_t* pf, hipStream_t stream) {
     const int64_t g = tile_blocks(s);
 #define ZERO_REDUCE_CASE(K) \
@@ -588,8 +571,8 @@ int zero_reduce_owned(void* dst, const void* const* srcs, int32_t n_ranks, int64
     if (rc != ZERO_OK || count == 0) return rc;
     uint16_t* d = (uint16_t*)dst;
     return dtype == ZERO_FP16
-               ? launch_reduce_n<ZERO_FP16, false>(d, rp, n_ranks, s, 0.0, nullptr, nullptr, stream)
-               : launch_reduce_n<ZERO_BF16, false>(d, rp, n_ranks, s, 0.0, nullptr, nullptr, stream);
+               ? launch_reduce_n<ZERO_FP16, false>(d, rp, n_ranks, s, 0.0f, nullptr, nullptr, stream)
+               : launch_reduce_n<ZERO_BF16, false>(d, rp, n_ranks, s, 0.0f, nullptr, nullptr, stream);
 }
 
 size_t zero_check_workspace_bytes(int64_t count) {
@@ -612,9 +595,9 @@ int zero_unscale_check_norm(const void* grad16, int64_t count, int32_t dtype, fl
     double* ps = (double*)(ws + L.sum_off[0]);
     uint32_t* pf = (uint32_t*)(ws + L.flag_off[0]);
     const uint16_t* g = (const uint16_t*)grad16;
-    const double inv = (double)inv_scale;
-    rc = dtype == ZERO_FP16 ? launch(check_kernel<ZERO_FP16>, blocks, stream, g, s, inv, ps, pf)
-                            : launch(check_kernel<ZERO_BF16>, blocks, stream, g, s, inv, ps, pf);
+    rc = dtype == ZERO_FP16
+             ? launch(check_kernel<ZERO_FP16>, blocks, stream, g, s, inv_scale, ps, pf)
+             : launch(check_kernel<ZERO_BF16>, blocks, stream, g, s, inv_scale, ps, pf);
     if (rc != ZERO_OK) return rc;
     return fold_into(ws, L, inv_scale, accumulate, res, stream);
 }
@@ -634,10 +617,9 @@ int zero_reduce_check_owned(void* dst, const void* const* srcs, int32_t n_ranks,
     double* ps = (double*)(ws + L.sum_off[0]);
     uint32_t* pf = (uint32_t*)(ws + L.flag_off[0]);
     uint16_t* d = (uint16_t*)dst;
-    const double inv = (double)inv_scale;
     rc = dtype == ZERO_FP16
-             ? launch_reduce_n<ZERO_FP16, true>(d, rp, n_ranks, s, inv, ps, pf, stream)
-             : launch_reduce_n<ZERO_BF16, true>(d, rp, n_ranks, s, inv, ps, pf, stream);
+             ? launch_reduce_n<ZERO_FP16, true>(d, rp, n_ranks, s, inv_scale, ps, pf, stream)
+             : launch_reduce_n<ZERO_BF16, true>(d, rp, n_ranks, s, inv_scale, ps, pf, stream);
     if (rc != ZERO_OK) return rc;
     return fold_into(ws, L, inv_scale, accumulate, res, stream);
 }
