@@ -14,10 +14,17 @@
 namespace {
 
 constexpr int kThreads = 256;          // 4 wave64s per block
-constexpr int kVec = 8;                // elements per lane (one 128-bit 16-bit access)
-constexpr int kTile = kThreads * kVec; // elements per block
+constexpr int kVec = 8;                // elements per lane tile (one 128-bit 16-bit access)
+constexpr int kTile = kThreads * kVec; // elements per block and lane tile
 constexpr int kFold = 2048;            // partials folded per block per fold pass
 constexpr int kMaxStreamBlocks = 256 * 8;  // grid-stride kernels off the hot path
+// A launch's total thread count must stay below 2^32 (HIP truncates it
+// silently beyond that), so tile kernels are launched in pieces of at most
+// this many blocks; Split::blk0 carries the piece's first block.
+constexpr int64_t kMaxLaunchBlocks = int64_t(1) << 21;
+// LDS per CU on gfx950.  Dynamic LDS is used to cap how many blocks of a
+// streaming kernel share a CU (lds_for_blocks).
+constexpr unsigned kLdsPerCU = 160 * 1024;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -28,6 +35,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // walks its 8 elements with 16/32-bit accesses.
 struct Split {
     int64_t head, nvec, count;
+    int64_t blk0;      // global index of the launch's first block
     int aligned;
 };
 
@@ -59,8 +67,15 @@ __device__ __forceinline__ u32x4 pack8(const uint16_t* h) {
     for (int q = 0; q < 4; ++q) w[q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
     return w;
 }
-__device__ __forceinline__ int64_t lane_tile() {
-    return (int64_t)blockIdx.x * kThreads + threadIdx.x;
+// Global block index of a tile kernel launched in pieces.
+__device__ __forceinline__ int64_t block_id(const Split& s) {
+    return s.blk0 + (int64_t)blockIdx.x;
+}
+// Lane tile of lane threadIdx.x in the t-th of TPL block-wide rows of lane
+// tiles that block block_id(s) owns: consecutive lanes, consecutive tiles.
+template <int TPL = 1>
+__device__ __forceinline__ int64_t lane_tile(const Split& s, int t = 0) {
+    return (block_id(s) * TPL + t) * kThreads + threadIdx.x;
 }
 
 // ------------------------------------------------------------ host -------
@@ -90,6 +105,7 @@ inline int64_t vector_head(const void* const* p16, int n16, const void* const* p
 inline Split split_for(int64_t head, int64_t count) {
     Split s;
     s.count = count;
+    s.blk0 = 0;
     if (head < 0) {
         s.head = 0;
         s.nvec = 0;
@@ -103,10 +119,11 @@ inline Split split_for(int64_t head, int64_t count) {
     return s;
 }
 
-// Blocks of a tile kernel: one per 256 lane-tiles, at least one.
-inline int64_t tile_blocks(const Split& s) {
+// Blocks of a tile kernel whose lanes take TPL lane tiles each, at least one.
+inline int64_t tile_blocks(const Split& s, int tpl = 1) {
     const int64_t lanes = s.aligned ? s.nvec : (s.count + kVec - 1) / kVec;
-    const int64_t b = (lanes + kThreads - 1) / kThreads;
+    const int64_t per = (int64_t)kThreads * tpl;
+    const int64_t b = (lanes + per - 1) / per;
     return b < 1 ? 1 : b;
 }
 
@@ -115,19 +132,44 @@ inline int64_t max_tile_blocks(int64_t count) {
     return (count + kTile - 1) / kTile + 1;
 }
 
-// Launches `kernel` with its arguments converted to the kernel's parameter
-// types and returns this launch's own status (not a stale thread-local one).
+// Dynamic LDS bytes that leave room for exactly `b` resident blocks per CU
+// (0: no cap).  Streaming kernels with many concurrent HBM streams run
+// faster on MI355X with fewer waves in flight: fewer DRAM rows are open at
+// once, while enough bytes stay in flight to cover the latency.
+inline unsigned lds_for_blocks(int b) {
+    return b >= 8 ? 0u : kLdsPerCU / (unsigned)(b + 1) + 2048u;
+}
+
+// Launches `kernel` on `grid` blocks with `lds` bytes of dynamic LDS, its
+// arguments converted to the kernel's parameter types, and returns this
+// launch's own status (not a stale thread-local one).
 template <typename... KArgs, typename... Args>
-inline int launch(void (*kernel)(KArgs...), int64_t grid, hipStream_t stream, Args... args) {
+inline int launch(void (*kernel)(KArgs...), int64_t grid, unsigned lds, hipStream_t stream,
+                  Args... args) {
     static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
-    if (grid < 1 || grid > 0x7FFFFFFF) return ZERO_ERANGE;
+    if (grid < 1 || grid > kMaxLaunchBlocks) return ZERO_ERANGE;
     std::tuple<KArgs...> packed(static_cast<KArgs>(args)...);
     void* ptrs[sizeof...(KArgs)];
     int i = 0;
     std::apply([&](auto&... a) { ((ptrs[i++] = (void*)&a), ...); }, packed);
-    const hipError_t err =
-        hipLaunchKernel((const void*)kernel, dim3((unsigned)grid), dim3(kThreads), ptrs, 0, stream);
+    const hipError_t err = hipLaunchKernel((const void*)kernel, dim3((unsigned)grid),
+                                           dim3(kThreads), ptrs, lds, stream);
     return err == hipSuccess ? ZERO_OK : ZERO_EDEVICE;
+}
+
+// Runs a tile kernel over `blocks` blocks as launches of at most
+// kMaxLaunchBlocks, in order on one stream: go(piece, grid) launches one
+// piece, whose Split has blk0 set.
+template <typename F>
+inline int launch_pieces(const Split& s, int64_t blocks, F&& go) {
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxLaunchBlocks) {
+        Split piece = s;
+        piece.blk0 = b0;
+        const int64_t g = blocks - b0 < kMaxLaunchBlocks ? blocks - b0 : kMaxLaunchBlocks;
+        const int rc = go(piece, g);
+        if (rc != ZERO_OK) return rc;
+    }
+    return ZERO_OK;
 }
 
 }  // namespace

@@ -84,15 +84,15 @@ __global__ void __launch_bounds__(kThreads)
 flat_gather_kernel(uint16_t* __restrict__ flat, Split s, const zero_tensor_desc* __restrict__ descs,
                    int64_t n_descs) {
     __shared__ int64_t s_first;
-    const int64_t base = s.aligned ? s.head + (int64_t)blockIdx.x * kTile
-                                   : (int64_t)blockIdx.x * kTile;
-    if (threadIdx.x == 0) s_first = desc_at(descs, n_descs, blockIdx.x == 0 ? 0 : base);
+    const int64_t blk = block_id(s);
+    const int64_t base = s.aligned ? s.head + blk * kTile : blk * kTile;
+    if (threadIdx.x == 0) s_first = desc_at(descs, n_descs, blk == 0 ? 0 : base);
     __syncthreads();
     DescCursor cur;
     cur.d = descs;
     cur.n = n_descs;
     cur.load(s_first);
-    const int64_t i = lane_tile();
+    const int64_t i = lane_tile(s);
     const int64_t e0 = s.aligned ? s.head + i * kVec : i * kVec;
     const bool vec_lane = s.aligned && i < s.nvec;
     if (vec_lane || (!s.aligned && e0 < s.count)) {
@@ -108,7 +108,7 @@ flat_gather_kernel(uint16_t* __restrict__ flat, Split s, const zero_tensor_desc*
             }
         }
     }
-    if (s.aligned && blockIdx.x == 0) {      // head and tail, one element per lane
+    if (s.aligned && blk == 0) {             // head and tail, one element per lane
         const int t = threadIdx.x;
         int64_t e = -1;
         if (t < s.head) e = t;
@@ -151,15 +151,15 @@ __global__ void __launch_bounds__(kThreads)
 flat_scatter_kernel(const uint16_t* __restrict__ flat, Split s,
                     const zero_tensor_desc* __restrict__ descs, int64_t n_descs) {
     __shared__ int64_t s_first;
-    const int64_t base = s.aligned ? s.head + (int64_t)blockIdx.x * kTile
-                                   : (int64_t)blockIdx.x * kTile;
-    if (threadIdx.x == 0) s_first = desc_at(descs, n_descs, blockIdx.x == 0 ? 0 : base);
+    const int64_t blk = block_id(s);
+    const int64_t base = s.aligned ? s.head + blk * kTile : blk * kTile;
+    if (threadIdx.x == 0) s_first = desc_at(descs, n_descs, blk == 0 ? 0 : base);
     __syncthreads();
     DescCursor cur;
     cur.d = descs;
     cur.n = n_descs;
     cur.load(s_first);
-    const int64_t i = lane_tile();
+    const int64_t i = lane_tile(s);
     const int64_t e0 = s.aligned ? s.head + i * kVec : i * kVec;
     const bool vec_lane = s.aligned && i < s.nvec;
     if (vec_lane || (!s.aligned && e0 < s.count)) {
@@ -175,7 +175,7 @@ flat_scatter_kernel(const uint16_t* __restrict__ flat, Split s,
             }
         }
     }
-    if (s.aligned && blockIdx.x == 0) {      // head and tail, one element per lane
+    if (s.aligned && blk == 0) {             // head and tail, one element per lane
         const int t = threadIdx.x;
         int64_t e = -1;
         if (t < s.head) e = t;
@@ -203,7 +203,9 @@ int zero_flat_gather(void* flat, int64_t flat_count, const zero_tensor_desc* des
     if (!flat || (n_descs > 0 && !descs)) return ZERO_EINVAL;
     const void* p = flat;
     const Split s = split_for(vector_head(&p, 1, nullptr, 0), flat_count);
-    return launch(flat_gather_kernel, tile_blocks(s), stream, (uint16_t*)flat, s, descs, n_descs);
+    return launch_pieces(s, tile_blocks(s), [&](const Split& piece, int64_t grid) {
+        return launch(flat_gather_kernel, grid, 0, stream, (uint16_t*)flat, piece, descs, n_descs);
+    });
 }
 
 int zero_flat_scatter(const void* flat, int64_t flat_count, const zero_tensor_desc* descs,
@@ -213,8 +215,10 @@ int zero_flat_scatter(const void* flat, int64_t flat_count, const zero_tensor_de
     if (!flat || !descs) return ZERO_EINVAL;
     const void* p = flat;
     const Split s = split_for(vector_head(&p, 1, nullptr, 0), flat_count);
-    return launch(flat_scatter_kernel, tile_blocks(s), stream, (const uint16_t*)flat, s, descs,
-                  n_descs);
+    return launch_pieces(s, tile_blocks(s), [&](const Split& piece, int64_t grid) {
+        return launch(flat_scatter_kernel, grid, 0, stream, (const uint16_t*)flat, piece, descs,
+                      n_descs);
+    });
 }
 
 }  // extern "C"

@@ -3,19 +3,26 @@
 //
 // Every phase is a flat streaming pass over HBM, so the kernels are built
 // around the memory system, not the ALUs:
-//   * a lane owns one tile of 8 consecutive elements: one 128-bit load per
-//     16-bit stream and two per fp32 stream; consecutive lanes own
-//     consecutive tiles, so a wave64 moves 1 KiB (16-bit) or 2 KiB (fp32)
-//     per stream per instruction, fully coalesced;
-//   * one 256-lane block per 2048 elements, no grid-stride loop: the hardware
-//     dispatcher keeps every CU of the 8 XCDs fed with short-lived blocks and
-//     the whole chip sweeps the buffers front to back.  On MI355X this beats
-//     a persistent grid-stride grid by 15-25% for every stream mix measured
-//     here (copy, AdamW's 4-read/4-write mix, the N-rank reduce);
+//   * a lane tile is 8 consecutive elements: one 128-bit load per 16-bit
+//     stream and two per fp32 stream; consecutive lanes own consecutive
+//     tiles, so a wave64 moves 1 KiB (16-bit) or 2 KiB (fp32) per stream per
+//     instruction, fully coalesced;
+//   * one 256-lane block per 1 (AdamW, check) or 2 (reduce) block-wide rows
+//     of lane tiles, no grid-stride loop: the hardware dispatcher keeps every
+//     CU of the 8 XCDs fed with short-lived blocks and the whole chip sweeps
+//     the buffers front to back.  On MI355X this beats a persistent
+//     grid-stride grid by 15-25% for every stream mix measured here;
 //   * all of a lane's loads are issued before any arithmetic;
-//   * the reduce streams data that is never re-read, so it loads and stores
-//     non-temporally; AdamW updates master / m / v in place, where plain
-//     accesses measured faster;
+//   * the kernels with many concurrent streams (AdamW: 4 read + 4 write;
+//     the reduce: N + 1) cap the blocks resident per CU with dynamic LDS:
+//     fewer waves in flight keep fewer DRAM rows open at once, and enough
+//     bytes stay in flight to cover the latency (AdamW 6.10 -> 6.37 TB/s on
+//     the LLaMA-70B-shaped shard, where a math-free twin of its stream mix
+//     peaks at 6.35);
+//   * data read once (rank gradients, the reduced gradient in AdamW) is
+//     loaded non-temporally, and the reduce stores non-temporally; AdamW
+//     updates master / m / v in place with plain accesses, which measured
+//     faster;
 //   * reductions (norm, overflow flag) go lane -> wave (cross-lane shuffles)
 //     -> block (LDS) -> one partial per block -> fold passes of 2048 partials
 //     per block -> one finalize block.  No floating-point atomics: the result
@@ -119,7 +126,8 @@ template <int DT>
 __global__ void __launch_bounds__(kThreads)
 init_master_kernel(float* __restrict__ master, const uint16_t* __restrict__ p16, int64_t count) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = lane_tile(); i < count; i += stride) master[i] = to_f32<DT>(p16[i]);
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < count; i += stride)
+        master[i] = to_f32<DT>(p16[i]);
 }
 
 // ------------------------------------------------------------ reduce -------
@@ -130,42 +138,77 @@ __device__ __forceinline__ uint16_t reduce_one(const RankPtrs& src, int n_ranks,
     return from_f32<DT>(acc);
 }
 
+// One lane tile of the reduce: the NR ranks' 128-bit words w[] of 8
+// elements, fp32 additions in rank order from +0 (0 + -0 is +0, so the first
+// addition is kept), one rounding to 16 bits, stored at d; with CHECK the
+// reduced values also go into (sq, bad).
+template <int DT, int NR, bool CHECK>
+__device__ __forceinline__ void reduce_tile(const u32x4 (&w)[NR], uint16_t* d, float inv, double& sq,
+                                            uint32_t& bad) {
+    float acc[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) acc[k] = 0.0f + to_f32<DT>(half_of(w[0], k));
+#pragma unroll
+    for (int r = 1; r < NR; ++r) {
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) acc[k] = acc[k] + to_f32<DT>(half_of(w[r], k));
+    }
+    uint16_t h[kVec];
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+        h[k] = from_f32<DT>(acc[k]);
+        if (CHECK) check_acc<DT>(h[k], inv, sq, bad);
+    }
+    store_nt(d, pack8(h));
+}
+
+// Lane tiles per lane in the reduce, and resident blocks per CU for NR
+// ranks: about 32 of a lane's 128-bit loads in flight per SIMD-slot whatever
+// the rank count (measured on MI355X: 8 ranks 5.83 -> 5.92-6.11 TB/s with
+// 2 blocks per CU, 16 ranks 5.70 -> 5.88 TB/s with 1).
+constexpr int kReduceTiles = 2;
+constexpr int reduce_blocks_per_cu(int nr) { return nr >= 16 ? 1 : (16 / nr > 8 ? 8 : 16 / nr); }
+
 // Reduce of NR ranks; with CHECK also the overflow flag and squared norm of
-// the reduced values, one partial per block.  No __restrict__ on dst / src:
-// dst may be one of the sources (every element is read, then written, by the
-// same lane).
+// the reduced values, one partial per block.  Block b owns kReduceTiles
+// block-wide rows of lane tiles; a lane issues all its loads (kReduceTiles
+// x NR 128-bit words) before any arithmetic.  No __restrict__ on dst / src:
+// dst may be one of the sources (every element is read, then written, by
+// the same lane).
 template <int DT, int NR, bool CHECK>
 __global__ void __launch_bounds__(kThreads)
 reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, double* part_sum,
               uint32_t* part_flag) {
     double sq = 0.0;
     uint32_t bad = 0;
-    const int64_t i = lane_tile();
+    const int64_t blk = block_id(s);
     if (s.aligned) {
-        if (i < s.nvec) {
-            const int64_t e = s.head + i * kVec;
-            u32x4 w[NR];
+        if (lane_tile<kReduceTiles>(s, kReduceTiles - 1) < s.nvec) {   // every row in range
+            u32x4 w[kReduceTiles][NR];
 #pragma unroll
-            for (int r = 0; r < NR; ++r) w[r] = load_nt(src.p[r] + e);
-            // fp32 additions in rank order from +0 (0 + -0 is +0, so the first
-            // addition is kept), one rounding to 16 bits
-            float acc[kVec];
+            for (int t = 0; t < kReduceTiles; ++t) {
+                const int64_t e = s.head + lane_tile<kReduceTiles>(s, t) * kVec;
 #pragma unroll
-            for (int k = 0; k < kVec; ++k) acc[k] = 0.0f + to_f32<DT>(half_of(w[0], k));
-#pragma unroll
-            for (int r = 1; r < NR; ++r) {
-#pragma unroll
-                for (int k = 0; k < kVec; ++k) acc[k] = acc[k] + to_f32<DT>(half_of(w[r], k));
+                for (int r = 0; r < NR; ++r) w[t][r] = load_nt(src.p[r] + e);
             }
-            uint16_t h[kVec];
 #pragma unroll
-            for (int k = 0; k < kVec; ++k) {
-                h[k] = from_f32<DT>(acc[k]);
-                if (CHECK) check_acc<DT>(h[k], inv, sq, bad);
+            for (int t = 0; t < kReduceTiles; ++t)
+                reduce_tile<DT, NR, CHECK>(w[t], dst + s.head + lane_tile<kReduceTiles>(s, t) * kVec,
+                                           inv, sq, bad);
+        } else {
+#pragma unroll
+            for (int t = 0; t < kReduceTiles; ++t) {
+                const int64_t i = lane_tile<kReduceTiles>(s, t);
+                if (i < s.nvec) {
+                    const int64_t e = s.head + i * kVec;
+                    u32x4 w[NR];
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) w[r] = load_nt(src.p[r] + e);
+                    reduce_tile<DT, NR, CHECK>(w, dst + e, inv, sq, bad);
+                }
             }
-            store_nt(dst + e, pack8(h));
         }
-        if (blockIdx.x == 0) {
+        if (blk == 0) {
             const int t = threadIdx.x;
             int64_t e = -1;
             if (t < s.head) e = t;
@@ -178,17 +221,20 @@ reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, double* part_sum,
             }
         }
     } else {
-        for (int64_t e = i * kVec; e < (i + 1) * kVec && e < s.count; ++e) {
-            const uint16_t h = reduce_one<DT>(src, NR, e);
-            dst[e] = h;
-            if (CHECK) check_acc<DT>(h, inv, sq, bad);
+        for (int t = 0; t < kReduceTiles; ++t) {
+            const int64_t i = lane_tile<kReduceTiles>(s, t);
+            for (int64_t e = i * kVec; e < (i + 1) * kVec && e < s.count; ++e) {
+                const uint16_t h = reduce_one<DT>(src, NR, e);
+                dst[e] = h;
+                if (CHECK) check_acc<DT>(h, inv, sq, bad);
+            }
         }
     }
     if (CHECK) {
         block_sum_or(sq, bad);
         if (threadIdx.x == 0) {
-            part_sum[blockIdx.x] = sq;
-            part_flag[blockIdx.x] = bad;
+            part_sum[blk] = sq;
+            part_flag[blk] = bad;
         }
     }
 }
@@ -200,14 +246,14 @@ check_kernel(const uint16_t* __restrict__ g, Split s, float inv, double* __restr
              uint32_t* __restrict__ part_flag) {
     double sq = 0.0;
     uint32_t bad = 0;
-    const int64_t i = lane_tile();
+    const int64_t i = lane_tile(s);
     if (s.aligned) {
         if (i < s.nvec) {
             const u32x4 w = load_nt(g + s.head + i * kVec);
 #pragma unroll
             for (int k = 0; k < kVec; ++k) check_acc<DT>(half_of(w, k), inv, sq, bad);
         }
-        if (blockIdx.x == 0) {
+        if (block_id(s) == 0) {
             const int t = threadIdx.x;
             if (t < s.head) check_acc<DT>(g[t], inv, sq, bad);
             else if (t >= 64 && t < 64 + kVec && s.head + s.nvec * kVec + (t - 64) < s.count)
@@ -219,8 +265,8 @@ check_kernel(const uint16_t* __restrict__ g, Split s, float inv, double* __restr
     }
     block_sum_or(sq, bad);
     if (threadIdx.x == 0) {
-        part_sum[blockIdx.x] = sq;
-        part_flag[blockIdx.x] = bad;
+        part_sum[block_id(s)] = sq;
+        part_flag[block_id(s)] = bad;
     }
 }
 
@@ -304,30 +350,40 @@ __device__ __forceinline__ void adam_one(const AdamConsts& c, float inv, float c
     p16[e] = from_f32<DT>(o.p);
 }
 
+// Clip factor from the global squared norm: max_norm / (norm + 1e-6) when
+// that is below 1, else 1; off when max_norm <= 0.  fp64, rounded once.
+__device__ __forceinline__ float clip_coef(const AdamConsts& c, const zero_step_result* res) {
+    float coef = 1.0f;
+    if (c.max_norm > 0.0f) {
+        const double q = (double)c.max_norm / (sqrt(res->sumsq) + 1e-6);
+        if (q < 1.0) coef = (float)q;
+    }
+    return coef;
+}
+
 template <int DT>
 __global__ void __launch_bounds__(kThreads)
 adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restrict__ va,
              uint16_t* __restrict__ p16, const uint16_t* __restrict__ g16, Split s, AdamConsts c,
              const zero_step_result* __restrict__ res) {
     if (res->overflow) return;                       // skipped step: write nothing
-    const float inv = res->inv_scale;
-    float coef = 1.0f;
-    if (c.max_norm > 0.0f) {
-        const double q = (double)c.max_norm / (sqrt(res->sumsq) + 1e-6);
-        if (q < 1.0) coef = (float)q;
-    }
-    const int64_t i = lane_tile();
+    // The clip factor is computed after the tile's loads are issued, so its
+    // fp64 square root and division overlap the HBM latency (computed before
+    // the loads they cost ~3% of the kernel's time at 2 blocks per CU).
+    const int64_t i = lane_tile(s);
     if (!s.aligned) {
+        const float inv = res->inv_scale, coef = clip_coef(c, res);
         for (int64_t e = i * kVec; e < (i + 1) * kVec && e < s.count; ++e)
             adam_one<DT>(c, inv, coef, master, ma, va, p16, g16, e);
         return;
     }
     if (i < s.nvec) {
         const int64_t e = s.head + i * kVec;
-        const u32x4 gw = load_b128(g16 + e);
+        const u32x4 gw = load_nt(g16 + e);          // read once: non-temporal
         const f32x4 p0 = load_f4(master + e), p1 = load_f4(master + e + 4);
         const f32x4 m0 = load_f4(ma + e), m1 = load_f4(ma + e + 4);
         const f32x4 v0 = load_f4(va + e), v1 = load_f4(va + e + 4);
+        const float inv = res->inv_scale, coef = clip_coef(c, res);
         f32x4 po[2], mo[2], vo[2];
         uint16_t ph[kVec];
 #pragma unroll
@@ -351,7 +407,8 @@ adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restri
         store_f4(va + e + 4, vo[1]);
         store_b128(p16 + e, pack8(ph));
     }
-    if (blockIdx.x == 0) {
+    if (block_id(s) == 0) {
+        const float inv = res->inv_scale, coef = clip_coef(c, res);
         const int t = threadIdx.x;
         if (t < s.head) adam_one<DT>(c, inv, coef, master, ma, va, p16, g16, t);
         else if (t >= 64 && t < 64 + kVec && s.head + s.nvec * kVec + (t - 64) < s.count)
@@ -399,13 +456,13 @@ unsigned stream_grid(int64_t items) {
 int fold_into(char* ws, const Levels& L, float inv_scale, int32_t accumulate, zero_step_result* res,
               hipStream_t stream) {
     for (int l = 0; l + 1 < L.n; ++l) {
-        const int rc = launch(fold_kernel, L.parts[l + 1], stream, (const double*)(ws + L.sum_off[l]),
+        const int rc = launch(fold_kernel, L.parts[l + 1], 0, stream, (const double*)(ws + L.sum_off[l]),
                               (const uint32_t*)(ws + L.flag_off[l]), L.parts[l],
                               (double*)(ws + L.sum_off[l + 1]), (uint32_t*)(ws + L.flag_off[l + 1]));
         if (rc != ZERO_OK) return rc;
     }
     const int last = L.n - 1;
-    return launch(finalize_kernel, 1, stream, (const double*)(ws + L.sum_off[last]),
+    return launch(finalize_kernel, 1, 0, stream, (const double*)(ws + L.sum_off[last]),
                   (const uint32_t*)(ws + L.flag_off[last]), L.parts[last], inv_scale,
                   (int)(accumulate != 0), res);
 }
@@ -413,9 +470,13 @@ int fold_into(char* ws, const Levels& L, float inv_scale, int32_t accumulate, ze
 template <int DT, bool CHECK>
 int launch_reduce_n(uint16_t* dst, const RankPtrs& src, int n, const Split& s, float inv,
                     double* ps, uint32_t* pf, hipStream_t stream) {
-    const int64_t g = tile_blocks(s);
-#define ZERO_REDUCE_CASE(K) \
-    case K: return launch(reduce_kernel<DT, K, CHECK>, g, stream, dst, src, s, inv, ps, pf);
+    const int64_t blocks = tile_blocks(s, kReduceTiles);
+#define ZERO_REDUCE_CASE(K)                                                                    \
+    case K:                                                                                    \
+        return launch_pieces(s, blocks, [&](const Split& piece, int64_t g) {                   \
+            return launch(reduce_kernel<DT, K, CHECK>, g, lds_for_blocks(reduce_blocks_per_cu(K)), \
+                          stream, dst, src, piece, inv, ps, pf);                               \
+        });
     switch (n) {
         ZERO_REDUCE_CASE(1) ZERO_REDUCE_CASE(2) ZERO_REDUCE_CASE(3) ZERO_REDUCE_CASE(4)
         ZERO_REDUCE_CASE(5) ZERO_REDUCE_CASE(6) ZERO_REDUCE_CASE(7) ZERO_REDUCE_CASE(8)
@@ -559,8 +620,9 @@ int zero_init_master(float* master, const void* param16, int64_t count, int32_t 
     if (!master || !param16) return ZERO_EINVAL;
     const unsigned grid = stream_grid(count);
     const uint16_t* p = (const uint16_t*)param16;
-    return dtype == ZERO_FP16 ? launch(init_master_kernel<ZERO_FP16>, grid, stream, master, p, count)
-                              : launch(init_master_kernel<ZERO_BF16>, grid, stream, master, p, count);
+    return dtype == ZERO_FP16
+               ? launch(init_master_kernel<ZERO_FP16>, grid, 0, stream, master, p, count)
+               : launch(init_master_kernel<ZERO_BF16>, grid, 0, stream, master, p, count);
 }
 
 int zero_reduce_owned(void* dst, const void* const* srcs, int32_t n_ranks, int64_t count,
@@ -595,9 +657,11 @@ int zero_unscale_check_norm(const void* grad16, int64_t count, int32_t dtype, fl
     double* ps = (double*)(ws + L.sum_off[0]);
     uint32_t* pf = (uint32_t*)(ws + L.flag_off[0]);
     const uint16_t* g = (const uint16_t*)grad16;
-    rc = dtype == ZERO_FP16
-             ? launch(check_kernel<ZERO_FP16>, blocks, stream, g, s, inv_scale, ps, pf)
-             : launch(check_kernel<ZERO_BF16>, blocks, stream, g, s, inv_scale, ps, pf);
+    rc = launch_pieces(s, blocks, [&](const Split& piece, int64_t grid) {
+        return dtype == ZERO_FP16
+                   ? launch(check_kernel<ZERO_FP16>, grid, 0, stream, g, piece, inv_scale, ps, pf)
+                   : launch(check_kernel<ZERO_BF16>, grid, 0, stream, g, piece, inv_scale, ps, pf);
+    });
     if (rc != ZERO_OK) return rc;
     return fold_into(ws, L, inv_scale, accumulate, res, stream);
 }
@@ -611,7 +675,7 @@ int zero_reduce_check_owned(void* dst, const void* const* srcs, int32_t n_ranks,
     if (rc != ZERO_OK) return rc;
     rc = check_args(res, workspace, workspace_bytes, count, inv_scale);
     if (rc != ZERO_OK) return rc;
-    const int64_t blocks = tile_blocks(s);
+    const int64_t blocks = tile_blocks(s, kReduceTiles);
     const Levels L = levels_for(blocks);
     char* ws = (char*)workspace;
     double* ps = (double*)(ws + L.sum_off[0]);
@@ -649,11 +713,16 @@ int zero_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, void* para
     const int64_t blocks = tile_blocks(s);
     uint16_t* p16 = (uint16_t*)param16;
     const uint16_t* g16 = (const uint16_t*)grad16;
-    return dtype == ZERO_FP16
-               ? launch(adamw_kernel<ZERO_FP16>, blocks, stream, master, exp_avg, exp_avg_sq, p16,
-                        g16, s, c, res)
-               : launch(adamw_kernel<ZERO_BF16>, blocks, stream, master, exp_avg, exp_avg_sq, p16,
-                        g16, s, c, res);
+    // 2 resident blocks per CU: 6.10 -> 6.37 TB/s on the LLaMA-70B-shaped
+    // shard, 5.33 -> 5.84 TB/s on the 7B one (MI355X)
+    const unsigned lds = lds_for_blocks(2);
+    return launch_pieces(s, blocks, [&](const Split& piece, int64_t grid) {
+        return dtype == ZERO_FP16
+                   ? launch(adamw_kernel<ZERO_FP16>, grid, lds, stream, master, exp_avg,
+                            exp_avg_sq, p16, g16, piece, c, res)
+                   : launch(adamw_kernel<ZERO_BF16>, grid, lds, stream, master, exp_avg,
+                            exp_avg_sq, p16, g16, piece, c, res);
+    });
 }
 
 }  // extern "C"
