@@ -31,6 +31,9 @@
  *     stream).  None of them synchronises.  Any element offset is accepted;
  *     pointers that share their alignment modulo 16 bytes take the 128-bit
  *     vector path for everything but at most 7 leading and 7 trailing elements.
+ *   - Element counts are limited by memory only: a pass over more elements
+ *     than one launch's 32-bit grid holds (about 34e9) is issued as several
+ *     launches, in order, on the same stream.
  *   - Arguments are checked before anything is launched; a bad argument
  *     returns ZERO_EINVAL (or ZERO_ERANGE for sizes that overflow) and
  *     launches nothing.  A failed launch returns ZERO_EDEVICE.  No call

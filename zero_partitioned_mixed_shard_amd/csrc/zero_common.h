@@ -18,10 +18,11 @@ constexpr int kVec = 8;                // elements per lane tile (one 128-bit 16
 constexpr int kTile = kThreads * kVec; // elements per block and lane tile
 constexpr int kFold = 2048;            // partials folded per block per fold pass
 constexpr int kMaxStreamBlocks = 256 * 8;  // grid-stride kernels off the hot path
-// A launch's total thread count must stay below 2^32 (HIP truncates it
-// silently beyond that), so tile kernels are launched in pieces of at most
-// this many blocks; Split::blk0 carries the piece's first block.
-constexpr int64_t kMaxLaunchBlocks = int64_t(1) << 21;
+// A launch's total thread count must fit in 32 bits (the dispatch packet's
+// grid size; HIP truncates it silently beyond that), so tile kernels are
+// launched in pieces of at most this many blocks (34.4e9 elements at one lane
+// tile per lane); Split::blk0 carries the piece's first block.
+constexpr int64_t kMaxLaunchBlocks = (int64_t(1) << 32) / kThreads - 1;
 // LDS per CU on gfx950.  Dynamic LDS is used to cap how many blocks of a
 // streaming kernel share a CU (lds_for_blocks).
 constexpr unsigned kLdsPerCU = 160 * 1024;
