@@ -83,6 +83,9 @@ def parse():
                     help="separate allocations instead of one arena with spread placement")
     ap.add_argument("--min-gap-gib", type=float, default=0.0,
                     help="minimum distance between the AdamW streams' bases in the arena")
+    ap.add_argument("--write-back", action="store_true",
+                    help="buckets workload: also scatter the updated 16-bit flat buffer into "
+                         "per-parameter tensors after AdamW (zero_flat_scatter), timed as a phase")
     return ap.parse_args()
 
 
@@ -168,13 +171,18 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
     return shard, begin, end, padded, in_place
 
 
-def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
+def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
+                  write_back: bool = False):
     """The 10,000-tensor group with all N owners on this GPU, as the bench runs
     it: rank 0's gradient arrives as one separate device tensor per parameter
     (10,000 allocations) and is copied into rank 0's flat buffer bucket by
     bucket (zero_flat_gather, ZeRO-2 source walkthrough section 2.4
-    contiguous_gradients); ranks 1..N-1 arrive already flat.  Returns
-    (shard, copy_in, padded) where copy_in() enqueues the copy-in."""
+    contiguous_gradients); ranks 1..N-1 arrive already flat.  With write_back,
+    the parameters also live as one device tensor each (10,000 allocations)
+    and the updated flat 16-bit buffer is scattered into them after the step
+    (zero_flat_scatter, ZeRO-2 source walkthrough section 4.4).  Returns
+    (shard, copy_in, padded, write_back) where copy_in() / write_back()
+    enqueue the copies (write_back is None without the option)."""
     import torch
 
     from synth import inputs as I
@@ -208,9 +216,19 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
             Z.zero_flat_gather(flat0[a:z], descs)
 
     copy_in()
+    wb = None
+    if write_back:
+        params = [torch.empty(int(n), dtype=shard.param16.dtype, device="cuda") for n in wl.numels]
+        wb_descs = Z.tensor_descs(params, [int(o) for o in offs])
+
+        def wb():
+            Z.zero_flat_scatter(shard.param16, wb_descs)
+
+        wb()
+        shard.per_tensor_params = params
     torch.cuda.synchronize()
     shard.per_tensor_grads = grads
-    return shard, copy_in, padded
+    return shard, copy_in, padded, wb
 
 
 def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fused: bool = True):
@@ -280,7 +298,11 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     copy_in = None
+    write_back = None
     rr_info = None
+    if args.write_back and args.workload != "buckets":
+        print(json.dumps({"error": "--write-back applies to --workload buckets"}), file=sys.stderr)
+        sys.exit(2)
     if args.round_robin_owner is not None:
         shard, count_rr, n_owned, imbalance = build_round_robin(
             wl, args.round_robin_owner, arena=not args.no_arena,
@@ -289,9 +311,9 @@ def main():
         rr_info = {"owner": args.round_robin_owner, "owned_tensors": n_owned,
                    "owned_elems": count_rr, "largest_over_mean_owner": round(imbalance, 4)}
     elif args.workload == "buckets":
-        shard, copy_in, padded = build_buckets(wl, arena=not args.no_arena,
-                                               min_gap=int(args.min_gap_gib * 2 ** 30),
-                                               fused=not args.unfused)
+        shard, copy_in, padded, write_back = build_buckets(
+            wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
+            fused=not args.unfused, write_back=args.write_back)
         begin, end, in_place = 0, padded, False
     else:
         shard, begin, end, padded, in_place = build_shard(
@@ -301,14 +323,23 @@ def main():
     bufs = shard.rank_bufs
 
 
+    def one_step(marks=None):
+        if write_back:
+            shard.launch(bufs, marks)
+            write_back()
+            if marks:
+                marks[5].record()
+            return shard.finish()
+        return shard.step(bufs, marks=marks)
+
     for _ in range(args.warmup):
         Z.zero_partition_layout(wl.numels, wl.world, wl.align)
         if copy_in:
             copy_in()
-        shard.step(bufs)
+        one_step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     applied = 0
     infos = []
     torch.cuda.synchronize()
@@ -321,7 +352,7 @@ def main():
         ev[k][4].record()
         if copy_in:
             copy_in()
-        info = shard.step(bufs, marks=ev[k])
+        info = one_step(marks=ev[k])
         applied += info.applied
         infos.append(info)
     stop.record()
@@ -345,6 +376,9 @@ def main():
     if copy_in:
         ms["copy_in"] = [e[4].elapsed_time(e[0]) for e in ev]
         bytes_per["copy_in"] = 4
+    if write_back:
+        ms["write_back"] = [e[3].elapsed_time(e[5]) for e in ev]
+        bytes_per["write_back"] = 4
     phases = {}
     for k, v in ms.items():
         avg = float(np.mean(v))
@@ -371,7 +405,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{wl.name}-shaped owner-0 shard" if args.workload != "buckets" else
-                         "10,000-tensor group, all owners, copy-in + bucketed reduce + AdamW")
+                         "10,000-tensor group, all owners, copy-in + bucketed reduce + AdamW"
+                         + (" + write-back" if write_back else ""))
                         if rr_info is None else
                         f"{wl.name}-shaped, round-robin owner {rr_info['owner']} (whole tensors)",
             "round_robin": rr_info,

@@ -28,6 +28,10 @@ pytestmark = pytest.mark.gpu
 
 FP16, BF16 = 1, 2
 COUNTS = [0, 1, 7, 8, 9, 4095, 100003]
+# the reduce takes two block-wide rows of 256 lane tiles per block (4096
+# elements): a last block with one full row and an empty second row, and one
+# whose second row holds a single lane tile
+REDUCE_COUNTS = COUNTS + [10240, 6152]
 SPECIAL = {FP16: [0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x7BFF, 0xFBFF, 0x7B53, 0x7C00, 0xFC00,
                   0x7E00],
            BF16: [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x7F7F, 0xFF7F, 0x7F00, 0x7F80, 0xFF80,
@@ -90,7 +94,7 @@ def test_init_master(dtype):
 # ------------------------------------------------------------- reduce ------
 @pytest.mark.parametrize("dtype", [FP16, BF16])
 @pytest.mark.parametrize("n_ranks", [1, 2, 3, 8, 16])
-@pytest.mark.parametrize("count", COUNTS)
+@pytest.mark.parametrize("count", REDUCE_COUNTS)
 @pytest.mark.parametrize("offset", [0, 3])
 def test_reduce_parity(dtype, n_ranks, count, offset):
     rng = np.random.default_rng(1000 * dtype + 100 * n_ranks + count % 97 + offset)
@@ -183,7 +187,7 @@ def test_check_parity(dtype, count, offset, specials):
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])
 @pytest.mark.parametrize("n_ranks", [1, 3, 8, 16])
-@pytest.mark.parametrize("count", COUNTS + [10_000_019])
+@pytest.mark.parametrize("count", REDUCE_COUNTS + [10_000_019])
 @pytest.mark.parametrize("offset", [0, 3])
 def test_reduce_check_fused_parity(dtype, n_ranks, count, offset):
     """zero_reduce_check_owned = reduce then check; 10,000,019 elements need

@@ -18,6 +18,32 @@ __device__ __forceinline__ int64_t desc_at(const zero_tensor_desc* d, int64_t n,
     return lo - 1;
 }
 
+// Index of the last descriptor whose offset is <= e, or -1, found by one
+// whole wave: each round tests 64 evenly spaced descriptors at once and keeps
+// the interval between the last one at or below e and the next, so a table
+// of n entries costs ceil(log64 n) dependent loads (a binary search by one
+// thread: log2 n; on a 3,300-tensor bucket 2 loads instead of 12, which
+// matters because every block waits for it).  Every lane of the wave calls
+// it with the same e.  Every index it reads lies in [0, n), whatever the
+// table holds.
+__device__ __forceinline__ int64_t wave_desc_at(const zero_tensor_desc* d, int64_t n, int64_t e) {
+    const int lane = threadIdx.x & 63;
+    int64_t lo = 0, hi = n;           // lo == 0 or d[lo].offset <= e; answer in [lo - 1, hi)
+    while (hi - lo > 64) {
+        const int64_t step = (hi - lo + 63) / 64;
+        const int64_t j = lo + (int64_t)lane * step;
+        const bool le = j < hi && d[j].offset <= e;
+        const int c = __popcll(__ballot(le));
+        if (c == 0) return lo - 1;    // only when lo == 0: e lies before every tensor
+        const int64_t nhi = lo + (int64_t)c * step;
+        lo = lo + (int64_t)(c - 1) * step;
+        hi = nhi < hi ? nhi : hi;
+    }
+    const int64_t j = lo + lane;
+    const bool le = j < hi && d[j].offset <= e;
+    return lo + __popcll(__ballot(le)) - 1;
+}
+
 // A lane's view of the descriptor table: the tensor holding the flat
 // elements it is at, advanced forward only.
 struct DescCursor {
@@ -76,55 +102,6 @@ __device__ __forceinline__ u32x4 load8_unaligned(const uint16_t* p) {
     return o;
 }
 
-// Gather: one 8-element tile of the flat buffer per lane (aligned through
-// the head split); a tile inside one tensor takes the 128-bit path, others
-// go element by element.  Thread 0 finds the block's first tensor by binary
-// search; lanes walk forward from it.
-__global__ void __launch_bounds__(kThreads)
-flat_gather_kernel(uint16_t* __restrict__ flat, Split s, const zero_tensor_desc* __restrict__ descs,
-                   int64_t n_descs) {
-    __shared__ int64_t s_first;
-    const int64_t blk = block_id(s);
-    const int64_t base = s.aligned ? s.head + blk * kTile : blk * kTile;
-    if (threadIdx.x == 0) s_first = desc_at(descs, n_descs, blk == 0 ? 0 : base);
-    __syncthreads();
-    DescCursor cur;
-    cur.d = descs;
-    cur.n = n_descs;
-    cur.load(s_first);
-    const int64_t i = lane_tile(s);
-    const int64_t e0 = s.aligned ? s.head + i * kVec : i * kVec;
-    const bool vec_lane = s.aligned && i < s.nvec;
-    if (vec_lane || (!s.aligned && e0 < s.count)) {
-        cur.seek(e0);
-        const int64_t j0 = cur.index(e0);
-        if (vec_lane && j0 >= 0 && j0 + kVec <= cur.numel) {
-            store_nt(flat + e0, load8_unaligned(cur.ptr + j0));
-        } else {
-            for (int64_t e = e0; e < e0 + kVec && e < s.count; ++e) {
-                cur.seek(e);
-                const int64_t j = cur.index(e);
-                flat[e] = j >= 0 ? cur.ptr[j] : (uint16_t)0;
-            }
-        }
-    }
-    if (s.aligned && blk == 0) {             // head and tail, one element per lane
-        const int t = threadIdx.x;
-        int64_t e = -1;
-        if (t < s.head) e = t;
-        else if (t >= 64 && t < 64 + kVec && s.head + s.nvec * kVec + (t - 64) < s.count)
-            e = s.head + s.nvec * kVec + (t - 64);
-        if (e >= 0) {
-            DescCursor c2;
-            c2.d = descs;
-            c2.n = n_descs;
-            c2.load(desc_at(descs, n_descs, e));
-            const int64_t j = c2.index(e);
-            flat[e] = j >= 0 ? c2.ptr[j] : (uint16_t)0;
-        }
-    }
-}
-
 // 8 consecutive 16-bit values (packed in w) to a 2-byte aligned address:
 // one 16-byte store when the address is 4-byte aligned, else a 16-bit store,
 // a 12-byte store and a 16-bit store.  Only these 16 bytes are written.
@@ -145,37 +122,77 @@ __device__ __forceinline__ void store8_unaligned(uint16_t* p, u32x4 w) {
     p[7] = (uint16_t)(w[3] >> 16);
 }
 
-// Scatter: one 8-element tile of the flat buffer per lane (aligned through
-// the head split), the mirror of the gather.
-__global__ void __launch_bounds__(kThreads)
-flat_scatter_kernel(const uint16_t* __restrict__ flat, Split s,
-                    const zero_tensor_desc* __restrict__ descs, int64_t n_descs) {
+// Block-wide rows of lane tiles per block in the copy kernels: the block's
+// dependent lookups (the descriptor search, the first descriptor) are paid
+// once for 4 rows, and a lane has the loads of all 4 rows in flight at once.
+constexpr int kFlatRows = 4;
+
+// First descriptor at or below flat element e for the whole block (wave 0
+// searches, LDS broadcasts).  Every thread of the block calls it.
+__device__ __forceinline__ int64_t block_first_desc(const zero_tensor_desc* d, int64_t n, int64_t e) {
     __shared__ int64_t s_first;
-    const int64_t blk = block_id(s);
-    const int64_t base = s.aligned ? s.head + blk * kTile : blk * kTile;
-    if (threadIdx.x == 0) s_first = desc_at(descs, n_descs, blk == 0 ? 0 : base);
+    if (threadIdx.x < 64) {
+        const int64_t k = wave_desc_at(d, n, e);
+        if (threadIdx.x == 0) s_first = k;
+    }
     __syncthreads();
+    return s_first;
+}
+
+// Copy between the flat buffer and the tensors the descriptors name
+// (GATHER: tensors -> flat, zero where no tensor; else flat -> tensors).
+// A lane owns one 8-element tile in each of the block's kFlatRows rows
+// (aligned through the head split); a tile inside one tensor takes the
+// 128-bit path, others go element by element.  The lane walks the
+// descriptor table forward from the block's first tensor, issues the loads
+// of every row, then the stores.  Block 0 also does the head and tail
+// elements one per lane.  `flat` is only read when !GATHER.
+template <bool GATHER>
+__device__ __forceinline__ void flat_copy(uint16_t* flat, const Split& s,
+                                          const zero_tensor_desc* descs, int64_t n_descs) {
+    const int64_t blk = block_id(s);
+    const int64_t base = (s.aligned ? s.head : 0) + blk * (int64_t)kTile * kFlatRows;
     DescCursor cur;
     cur.d = descs;
     cur.n = n_descs;
-    cur.load(s_first);
-    const int64_t i = lane_tile(s);
-    const int64_t e0 = s.aligned ? s.head + i * kVec : i * kVec;
-    const bool vec_lane = s.aligned && i < s.nvec;
-    if (vec_lane || (!s.aligned && e0 < s.count)) {
+    cur.load(block_first_desc(descs, n_descs, blk == 0 ? 0 : base));
+    u32x4 v[kFlatRows];
+    uint16_t* to[kFlatRows];
+    bool fast[kFlatRows];
+#pragma unroll
+    for (int t = 0; t < kFlatRows; ++t) {
+        fast[t] = false;
+        const int64_t i = lane_tile<kFlatRows>(s, t);
+        const int64_t e0 = s.aligned ? s.head + i * kVec : i * kVec;
+        const bool vec_lane = s.aligned && i < s.nvec;
+        if (!vec_lane && (s.aligned || e0 >= s.count)) continue;
         cur.seek(e0);
         const int64_t j0 = cur.index(e0);
         if (vec_lane && j0 >= 0 && j0 + kVec <= cur.numel) {
-            store8_unaligned(cur.ptr + j0, load_nt(flat + e0));
+            if (GATHER) {
+                v[t] = load8_unaligned(cur.ptr + j0);
+                to[t] = flat + e0;
+            } else {
+                v[t] = load_nt(flat + e0);
+                to[t] = cur.ptr + j0;
+            }
+            fast[t] = true;
         } else {
             for (int64_t e = e0; e < e0 + kVec && e < s.count; ++e) {
                 cur.seek(e);
                 const int64_t j = cur.index(e);
-                if (j >= 0) cur.ptr[j] = flat[e];
+                if (GATHER) flat[e] = j >= 0 ? cur.ptr[j] : (uint16_t)0;
+                else if (j >= 0) cur.ptr[j] = flat[e];
             }
         }
     }
-    if (s.aligned && blk == 0) {             // head and tail, one element per lane
+#pragma unroll
+    for (int t = 0; t < kFlatRows; ++t) {
+        if (!fast[t]) continue;
+        if (GATHER) store_nt(to[t], v[t]);
+        else store8_unaligned(to[t], v[t]);
+    }
+    if (s.aligned && blk == 0) {
         const int t = threadIdx.x;
         int64_t e = -1;
         if (t < s.head) e = t;
@@ -187,9 +204,22 @@ flat_scatter_kernel(const uint16_t* __restrict__ flat, Split s,
             c2.n = n_descs;
             c2.load(desc_at(descs, n_descs, e));
             const int64_t j = c2.index(e);
-            if (j >= 0) c2.ptr[j] = flat[e];
+            if (GATHER) flat[e] = j >= 0 ? c2.ptr[j] : (uint16_t)0;
+            else if (j >= 0) c2.ptr[j] = flat[e];
         }
     }
+}
+
+__global__ void __launch_bounds__(kThreads)
+flat_gather_kernel(uint16_t* flat, Split s, const zero_tensor_desc* __restrict__ descs,
+                   int64_t n_descs) {
+    flat_copy<true>(flat, s, descs, n_descs);
+}
+
+__global__ void __launch_bounds__(kThreads)
+flat_scatter_kernel(const uint16_t* flat, Split s, const zero_tensor_desc* __restrict__ descs,
+                    int64_t n_descs) {
+    flat_copy<false>(const_cast<uint16_t*>(flat), s, descs, n_descs);
 }
 
 }  // namespace
@@ -203,7 +233,7 @@ int zero_flat_gather(void* flat, int64_t flat_count, const zero_tensor_desc* des
     if (!flat || (n_descs > 0 && !descs)) return ZERO_EINVAL;
     const void* p = flat;
     const Split s = split_for(vector_head(&p, 1, nullptr, 0), flat_count);
-    return launch_pieces(s, tile_blocks(s), [&](const Split& piece, int64_t grid) {
+    return launch_pieces(s, tile_blocks(s, kFlatRows), [&](const Split& piece, int64_t grid) {
         return launch(flat_gather_kernel, grid, 0, stream, (uint16_t*)flat, piece, descs, n_descs);
     });
 }
@@ -215,7 +245,7 @@ int zero_flat_scatter(const void* flat, int64_t flat_count, const zero_tensor_de
     if (!flat || !descs) return ZERO_EINVAL;
     const void* p = flat;
     const Split s = split_for(vector_head(&p, 1, nullptr, 0), flat_count);
-    return launch_pieces(s, tile_blocks(s), [&](const Split& piece, int64_t grid) {
+    return launch_pieces(s, tile_blocks(s, kFlatRows), [&](const Split& piece, int64_t grid) {
         return launch(flat_scatter_kernel, grid, 0, stream, (const uint16_t*)flat, piece, descs,
                       n_descs);
     });
