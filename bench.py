@@ -70,7 +70,7 @@ def parse():
                     choices=["toy", "bert", "llama7b", "llama70b", "buckets"])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (e.g. under a profiler)")
-    ap.add_argument("--cpu-seconds", type=float, default=2.0,
+    ap.add_argument("--cpu-seconds", type=float, default=1.5,
                     help="wall-clock budget of the CPU oracle leg")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (for HBM counter scaling)")
@@ -126,15 +126,23 @@ def cpu_baseline(wl, begin: int, seconds: float) -> dict:
         oracle.adamw(*v, red[a:z], wl.dtype, inv, sumsq, 0, hp, t)
 
     steps = 0
+    phase = {"reduce": 0.0, "check": 0.0, "adamw": 0.0}
     t0 = time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
         while True:
+            ta = time.perf_counter()
             list(ex.map(reduce_part, bounds))
+            tb = time.perf_counter()
             parts_ = list(ex.map(check_part, bounds))
             flag = max(p[0] for p in parts_)
             sumsq = sum(p[1] for p in parts_)
+            tc = time.perf_counter()
             steps += 1
             list(ex.map(adam_part, [(b, sumsq, steps) for b in bounds]))
+            td = time.perf_counter()
+            phase["reduce"] += tb - ta
+            phase["check"] += tc - tb
+            phase["adamw"] += td - tc
             assert flag == 0
             if time.perf_counter() - t0 >= seconds and steps >= 2:
                 break
@@ -142,7 +150,8 @@ def cpu_baseline(wl, begin: int, seconds: float) -> dict:
     return {"value": n * steps / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} owned elements of the same workload (N={wl.world} ranks), "
                       f"{steps} full oracle steps (reduce, check, AdamW) in {dt:.2f} s wall "
-                      f"on {threads} threads"}
+                      f"on {threads} threads (about {dt * threads:.0f} core-seconds)",
+            "phase_params_per_s": {k: round(n * steps / v, 1) for k, v in phase.items()}}
 
 
 def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
