@@ -72,6 +72,40 @@ def test_gather_scatter_parity(case):
         assert np.array_equal(to_np16(t), w)
 
 
+@pytest.mark.parametrize("mem_gap_max", [0, 3, 9])
+def test_views_of_one_buffer(mem_gap_max):
+    """Tensors that are views into one device buffer at arbitrary element
+    offsets, some back to back in memory with different misalignments: the
+    copy kernels share 16-byte chunks between lanes whose tiles are
+    consecutive in memory, whichever tensor they belong to.  The scatter must
+    write every view's elements exactly and leave the elements between views
+    untouched."""
+    rng = np.random.default_rng(100 + mem_gap_max)
+    sizes = [int(x) for x in rng.integers(1, 3000, 300)] + [1] * 40 + [9, 17, 2049, 5000]
+    rng.shuffle(sizes)
+    pos, cur = [], int(rng.integers(0, 8))
+    for n in sizes:
+        pos.append(cur)
+        cur += n + int(rng.integers(0, mem_gap_max + 1))
+    backing_host = rng.integers(0, 65536, cur + 8).astype(np.uint16)
+    backing = torch.from_numpy(backing_host.view(np.int16)).cuda().view(torch.bfloat16)
+    dev = [backing[p:p + n] for p, n in zip(pos, sizes)]
+    host = [backing_host[p:p + n].copy() for p, n in zip(pos, sizes)]
+    offs, count = _layout_with_gaps(sizes, rng, 5)
+    descs = Z.tensor_descs(dev, offs)
+    flat = torch.full((count,), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    Z.zero_flat_gather(flat, descs)
+    assert np.array_equal(to_np16(flat), oracle.flat_gather(host, offs, count))
+    new_flat = rng.integers(0, 65536, count).astype(np.uint16)
+    d_flat = torch.from_numpy(new_flat.view(np.int16)).cuda().view(torch.bfloat16)
+    Z.zero_flat_scatter(d_flat, descs)
+    back = oracle.flat_scatter(new_flat, offs, sizes)
+    want = backing_host.copy()
+    for p, n, w in zip(pos, sizes, back):
+        want[p:p + n] = w
+    assert np.array_equal(to_np16(backing), want)
+
+
 def test_invalid_arguments():
     flat = torch.zeros(16, dtype=torch.bfloat16, device="cuda")
     L = Z.lib()

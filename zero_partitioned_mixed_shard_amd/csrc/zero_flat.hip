@@ -6,6 +6,16 @@
 
 namespace {
 
+// Tensor pointers are read from the descriptor table, so the compiler cannot
+// tell that they point to global memory and would emit flat (generic)
+// accesses, whose completion is counted together with LDS and cross-lane
+// operations; these types make them global accesses.
+typedef __attribute__((address_space(1))) uint16_t g_u16;
+typedef __attribute__((address_space(1))) const u32x4 g_cu32x4;
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) uint32_t g_u32;
+typedef __attribute__((address_space(1))) uint64_t g_u64;
+
 // ------------------------------------------- flat <-> tensors (copy) -------
 // Last descriptor whose offset is <= e, or -1.
 __device__ __forceinline__ int64_t desc_at(const zero_tensor_desc* d, int64_t n, int64_t e) {
@@ -49,7 +59,7 @@ __device__ __forceinline__ int64_t wave_desc_at(const zero_tensor_desc* d, int64
 struct DescCursor {
     const zero_tensor_desc* d;
     int64_t n, k, off, numel, next;
-    uint16_t* ptr;
+    g_u16* ptr;
 
     __device__ __forceinline__ void load(int64_t kk) {
         k = kk;
@@ -57,7 +67,7 @@ struct DescCursor {
         off = 0;
         numel = 0;
         if (k >= 0) {
-            ptr = (uint16_t*)d[k].ptr;
+            ptr = (g_u16*)d[k].ptr;
             off = d[k].offset;
             numel = d[k].numel;
         }
@@ -73,16 +83,9 @@ struct DescCursor {
     }
 };
 
-// 8 consecutive 16-bit values starting at a 2-byte aligned address, read as
-// the two aligned 16-byte chunks that hold them.  Both chunks lie in the
-// pages of the first and last value, so nothing outside them is touched.
-__device__ __forceinline__ u32x4 load8_unaligned(const uint16_t* p) {
-    const uintptr_t a = (uintptr_t)p;
-    const u32x4* c = (const u32x4*)(a & ~(uintptr_t)15);
-    const int sh = (int)((a & 15) >> 1);     // 0..7 elements into the first chunk
-    const u32x4 c0 = __builtin_nontemporal_load(c);
-    if (sh == 0) return c0;
-    const u32x4 c1 = __builtin_nontemporal_load(c + 1);
+// The 8 16-bit values starting at element sh (0..7) of the 16 held in the
+// aligned chunks c0, c1 (c0 first).
+__device__ __forceinline__ u32x4 window8(u32x4 c0, u32x4 c1, int sh) {
     const uint32_t w[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
     u32x4 o;
     switch (sh) {
@@ -102,24 +105,43 @@ __device__ __forceinline__ u32x4 load8_unaligned(const uint16_t* p) {
     return o;
 }
 
-// 8 consecutive 16-bit values (packed in w) to a 2-byte aligned address:
-// one 16-byte store when the address is 4-byte aligned, else a 16-bit store,
-// a 12-byte store and a 16-bit store.  Only these 16 bytes are written.
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
+// The next lane's copy of x (lane 63 gets 0): a DPP wave shift, which moves
+// data between lanes in the VALU without the LDS crossbar.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x130 /* wave_shl:1 */, 0xF, 0xF,
+                                                 false);
+}
 
-__device__ __forceinline__ void store8_unaligned(uint16_t* p, u32x4 w) {
-    if (((uintptr_t)p & 3) == 0) {
-        *reinterpret_cast<u32x4_a4*>(p) = w;
-        return;
+// Stores elements [first, first + n) (n <= 7) of the 8 packed in w to
+// p[0, n) with at most four naturally aligned stores (2, 4 and 8 bytes).
+__device__ __forceinline__ void store_elems(g_u16* p, u32x4 w, int first, int n) {
+    const u32x4 zero = {0, 0, 0, 0};
+    u32x4 u = window8(w, zero, first);     // element `first` first
+    if (n > 0 && ((uintptr_t)p & 2)) {
+        *p = (uint16_t)(u[0] & 0xFFFFu);
+        u = window8(u, zero, 1);
+        p += 1;
+        n -= 1;
     }
-    p[0] = (uint16_t)(w[0] & 0xFFFFu);
-    u32x3_a4 mid;
-    mid[0] = __builtin_amdgcn_alignbit(w[1], w[0], 16);
-    mid[1] = __builtin_amdgcn_alignbit(w[2], w[1], 16);
-    mid[2] = __builtin_amdgcn_alignbit(w[3], w[2], 16);
-    *reinterpret_cast<u32x3_a4*>(p + 1) = mid;
-    p[7] = (uint16_t)(w[3] >> 16);
+    if (n >= 2 && ((uintptr_t)p & 4)) {
+        *(g_u32*)p = u[0];
+        u = u32x4{u[1], u[2], u[3], 0};
+        p += 2;
+        n -= 2;
+    }
+    if (n >= 4) {
+        *(g_u64*)p = (uint64_t)u[0] | ((uint64_t)u[1] << 32);
+        u = u32x4{u[2], u[3], 0, 0};
+        p += 4;
+        n -= 4;
+    }
+    if (n >= 2) {
+        *(g_u32*)p = u[0];
+        u = u32x4{u[1], u[2], u[3], 0};
+        p += 2;
+        n -= 2;
+    }
+    if (n >= 1) *p = (uint16_t)(u[0] & 0xFFFFu);
 }
 
 // Block-wide rows of lane tiles per block in the copy kernels: the block's
@@ -142,43 +164,58 @@ __device__ __forceinline__ int64_t block_first_desc(const zero_tensor_desc* d, i
 // Copy between the flat buffer and the tensors the descriptors name
 // (GATHER: tensors -> flat, zero where no tensor; else flat -> tensors).
 // A lane owns one 8-element tile in each of the block's kFlatRows rows
-// (aligned through the head split); a tile inside one tensor takes the
-// 128-bit path, others go element by element.  The lane walks the
-// descriptor table forward from the block's first tensor, issues the loads
-// of every row, then the stores.  Block 0 also does the head and tail
-// elements one per lane.  `flat` is only read when !GATHER.
+// (aligned through the head split); a tile inside one tensor is "fast", the
+// others go element by element.  The lane walks the descriptor table forward
+// from the block's first tensor.  `flat` is only read when !GATHER.
+//
+// The tensor side of a fast tile is in general not 16-byte aligned (sh
+// elements into its aligned chunk).  Consecutive lanes of a row hold
+// consecutive tiles, so when the next lane's tile is the next 8 elements of
+// the same tensor (known from the lane's own tile: 8 more elements remain in
+// the tensor and the next lane is a vector lane of the row) the two tiles
+// sit in consecutive memory, and the lanes share chunks:
+//   gather: each lane loads its own first chunk and takes the second from
+//     the next lane (a DPP lane shift); a lane whose next tile lies
+//     elsewhere loads its second chunk itself;
+//   scatter: each lane stores the aligned chunk that holds its last sh and
+//     the next lane's first 8 - sh elements; a lane whose next tile lies
+//     elsewhere stores its last sh elements one by one, and a lane whose
+//     previous tile lies elsewhere stores its first 8 - sh (the same test,
+//     seen from the other lane, so every element is written exactly once).
+// Only the 16-byte chunks that hold a tile's own elements are read, and only
+// its tensor's elements are written.  All loads of all rows are issued
+// before the stores.  Block 0 also does the head and tail elements one per
+// lane.
 template <bool GATHER>
 __device__ __forceinline__ void flat_copy(uint16_t* flat, const Split& s,
                                           const zero_tensor_desc* descs, int64_t n_descs) {
     const int64_t blk = block_id(s);
     const int64_t base = (s.aligned ? s.head : 0) + blk * (int64_t)kTile * kFlatRows;
+    const int lane = threadIdx.x & 63;
     DescCursor cur;
     cur.d = descs;
     cur.n = n_descs;
     cur.load(block_first_desc(descs, n_descs, blk == 0 ? 0 : base));
-    u32x4 v[kFlatRows];
-    uint16_t* to[kFlatRows];
-    bool fast[kFlatRows];
+    bool fast[kFlatRows], next_ok[kFlatRows], prev_ok[kFlatRows];
+    int64_t e0[kFlatRows];
+    uintptr_t q[kFlatRows];                 // tensor-side address of a fast tile
 #pragma unroll
     for (int t = 0; t < kFlatRows; ++t) {
-        fast[t] = false;
+        fast[t] = next_ok[t] = prev_ok[t] = false;
+        q[t] = 0;
         const int64_t i = lane_tile<kFlatRows>(s, t);
-        const int64_t e0 = s.aligned ? s.head + i * kVec : i * kVec;
+        e0[t] = s.aligned ? s.head + i * kVec : i * kVec;
         const bool vec_lane = s.aligned && i < s.nvec;
-        if (!vec_lane && (s.aligned || e0 >= s.count)) continue;
-        cur.seek(e0);
-        const int64_t j0 = cur.index(e0);
+        if (!vec_lane && (s.aligned || e0[t] >= s.count)) continue;
+        cur.seek(e0[t]);
+        const int64_t j0 = cur.index(e0[t]);
         if (vec_lane && j0 >= 0 && j0 + kVec <= cur.numel) {
-            if (GATHER) {
-                v[t] = load8_unaligned(cur.ptr + j0);
-                to[t] = flat + e0;
-            } else {
-                v[t] = load_nt(flat + e0);
-                to[t] = cur.ptr + j0;
-            }
             fast[t] = true;
+            q[t] = (uintptr_t)(cur.ptr + j0);
+            next_ok[t] = lane != 63 && j0 + 2 * kVec <= cur.numel && i + 1 < s.nvec;
+            prev_ok[t] = lane != 0 && j0 >= kVec;
         } else {
-            for (int64_t e = e0; e < e0 + kVec && e < s.count; ++e) {
+            for (int64_t e = e0[t]; e < e0[t] + kVec && e < s.count; ++e) {
                 cur.seek(e);
                 const int64_t j = cur.index(e);
                 if (GATHER) flat[e] = j >= 0 ? cur.ptr[j] : (uint16_t)0;
@@ -186,11 +223,52 @@ __device__ __forceinline__ void flat_copy(uint16_t* flat, const Split& s,
             }
         }
     }
+    u32x4 v[kFlatRows];
+    if (GATHER) {
+        u32x4 c1[kFlatRows];
 #pragma unroll
-    for (int t = 0; t < kFlatRows; ++t) {
-        if (!fast[t]) continue;
-        if (GATHER) store_nt(to[t], v[t]);
-        else store8_unaligned(to[t], v[t]);
+        for (int t = 0; t < kFlatRows; ++t) {
+            g_cu32x4* c = (g_cu32x4*)(q[t] & ~(uintptr_t)15);
+            const int sh = (int)((q[t] & 15) >> 1);
+            v[t] = u32x4{0, 0, 0, 0};
+            c1[t] = u32x4{0, 0, 0, 0};
+            if (fast[t]) v[t] = __builtin_nontemporal_load(c);
+            if (fast[t] && sh != 0 && !next_ok[t]) c1[t] = __builtin_nontemporal_load(c + 1);
+        }
+#pragma unroll
+        for (int t = 0; t < kFlatRows; ++t) {
+            u32x4 nx;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) nx[w] = from_next_lane(v[t][w]);
+            if (next_ok[t]) c1[t] = nx;
+            v[t] = window8(v[t], c1[t], (int)((q[t] & 15) >> 1));
+        }
+#pragma unroll
+        for (int t = 0; t < kFlatRows; ++t)
+            if (fast[t]) store_nt(flat + e0[t], v[t]);
+    } else {
+#pragma unroll
+        for (int t = 0; t < kFlatRows; ++t) {
+            v[t] = u32x4{0, 0, 0, 0};
+            if (fast[t]) v[t] = load_nt(flat + e0[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < kFlatRows; ++t) {
+            u32x4 nx;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) nx[w] = from_next_lane(v[t][w]);
+            if (!fast[t]) continue;
+            g_u16* p = (g_u16*)q[t];
+            const int m = (int)((q[t] & 15) >> 1);
+            if (m == 0) {
+                *(g_u32x4*)p = v[t];
+                continue;
+            }
+            g_u16* c = (g_u16*)(q[t] & ~(uintptr_t)15);
+            if (next_ok[t]) *(g_u32x4*)(c + kVec) = window8(v[t], nx, kVec - m);
+            else store_elems(c + kVec, v[t], kVec - m, m);
+            if (!prev_ok[t]) store_elems(p, v[t], 0, kVec - m);
+        }
     }
     if (s.aligned && blk == 0) {
         const int t = threadIdx.x;
