@@ -190,8 +190,8 @@ def test_check_parity(dtype, count, offset, specials):
 @pytest.mark.parametrize("count", REDUCE_COUNTS + [10_000_019])
 @pytest.mark.parametrize("offset", [0, 3])
 def test_reduce_check_fused_parity(dtype, n_ranks, count, offset):
-    """zero_reduce_check_owned = reduce then check; 10,000,019 elements need
-    two fold levels of block partials."""
+    """zero_reduce_check_owned = reduce then check; 10,000,019 elements give
+    2,442 block partials, folded by the one-block final pass."""
     if count > 1_000_000 and n_ranks not in (8, 16):
         pytest.skip("large size only at the workload rank counts")
     rng = np.random.default_rng(7 * dtype + 31 * n_ranks + count % 101 + offset)
@@ -210,6 +210,32 @@ def test_reduce_check_fused_parity(dtype, n_ranks, count, offset):
     assert r.overflow == flag and r.inv_scale == inv
     if not flag:
         assert r.sumsq == pytest.approx(sumsq, rel=1e-12, abs=0)
+
+
+@pytest.mark.parametrize("entry", ["fused", "check"])
+def test_norm_through_fold_levels(entry):
+    """Past 16,384 block partials the partials go through a fold pass before
+    the final one: the fused reduce+check over 70,000,019 elements (17,090
+    partials) and the check over 40,000,003 (19,532 partials), against the
+    oracle's norm."""
+    dtype = BF16
+    rng = np.random.default_rng(23 if entry == "fused" else 29)
+    count = 70_000_019 if entry == "fused" else 40_000_003
+    n_ranks = 8 if entry == "fused" else 1
+    host = [_rand16(count, dtype, rng) for _ in range(n_ranks)]
+    want = oracle.reduce(host, dtype) if entry == "fused" else host[0]
+    res = _res_tensor()
+    inv = 2.0 ** -3
+    if entry == "fused":
+        dst = _dev16(np.zeros(count, np.uint16), dtype, 3)
+        Z.zero_reduce_check_owned(dst, [_dev16(h, dtype, 3) for h in host], inv, res, _ws(count))
+        assert_bits16_equal(to_np16(dst), want, dtype, "fused reduce, fold levels")
+    else:
+        Z.zero_unscale_check_norm(_dev16(host[0], dtype, 3), inv, res, _ws(count))
+    r = Z.read_result(res)
+    flag, sumsq = oracle.check(want, dtype, inv)
+    assert r.overflow == flag == 0
+    assert r.sumsq == pytest.approx(sumsq, rel=1e-12, abs=0)
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])

@@ -17,6 +17,7 @@ constexpr int kThreads = 256;          // 4 wave64s per block
 constexpr int kVec = 8;                // elements per lane tile (one 128-bit 16-bit access)
 constexpr int kTile = kThreads * kVec; // elements per block and lane tile
 constexpr int kFold = 2048;            // partials folded per block per fold pass
+constexpr int kFinal = 16384;          // partials the one-block final pass takes
 constexpr int kMaxStreamBlocks = 256 * 8;  // grid-stride kernels off the hot path
 // A launch's total thread count must fit in 32 bits (the dispatch packet's
 // grid size; HIP truncates it silently beyond that), so tile kernels are
