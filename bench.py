@@ -83,6 +83,9 @@ def parse():
                     help="separate allocations instead of one arena with spread placement")
     ap.add_argument("--min-gap-gib", type=float, default=0.0,
                     help="minimum distance between the AdamW streams' bases in the arena")
+    ap.add_argument("--graph", action="store_true",
+                    help="keep the loss scaler and step count on the device and replay one "
+                         "captured HIP graph per step (no host round trip between steps)")
     ap.add_argument("--write-back", action="store_true",
                     help="buckets workload: also scatter the updated 16-bit flat buffer into "
                          "per-parameter tensors after AdamW (zero_flat_scatter), timed as a phase")
@@ -154,7 +157,8 @@ def cpu_baseline(wl, begin: int, seconds: float) -> dict:
             "phase_params_per_s": {k: round(n * steps / v, 1) for k, v in phase.items()}}
 
 
-def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
+def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
+                device_control: bool = False):
     """Owner 0's shard of `wl` as the bench runs it: state, reduced gradient
     and the N rank buffers (the LLaMA-70B shard reduces in place into rank 0's
     buffer), initial 16-bit weights and one gradient batch generated on the
@@ -172,7 +176,8 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
                       beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
                       window=wl.window, in_place_rank=0 if in_place else None, fused=fused,
-                      own_ranks=True, world=wl.world, arena=arena, min_gap=min_gap)
+                      own_ranks=True, world=wl.world, arena=arena, min_gap=min_gap,
+                      device_control=device_control)
     shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16))
     for r, buf in enumerate(shard.rank_bufs):
         I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded, out=buf)
@@ -181,7 +186,7 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True):
 
 
 def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
-                  write_back: bool = False):
+                  write_back: bool = False, device_control: bool = False):
     """The 10,000-tensor group with all N owners on this GPU, as the bench runs
     it: rank 0's gradient arrives as one separate device tensor per parameter
     (10,000 allocations) and is copied into rank 0's flat buffer bucket by
@@ -207,7 +212,7 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                       eps=wl.eps, weight_decay=wl.weight_decay, max_grad_norm=wl.clip,
                       scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window,
                       windows=windows, fused=fused, own_ranks=True, world=wl.world,
-                      arena=arena, min_gap=min_gap)
+                      arena=arena, min_gap=min_gap, device_control=device_control)
     shard.load_param16(I.device_param16(wl, offs, 0, padded, out=shard.param16))
     for r, buf in enumerate(shard.rank_bufs):
         I.device_rank_grad(wl, 1, wl.scale0, r, 0, padded, padded, out=buf)
@@ -240,7 +245,8 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
     return shard, copy_in, padded, wb
 
 
-def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fused: bool = True):
+def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fused: bool = True,
+                      device_control: bool = False):
     """Round-robin inter-tensor ownership (ZeRO 优化器, "参数分配策略"): this
     owner holds the whole tensors i with i mod N == owner, packed back to back
     (state only for what it owns); each tensor is reduced to it on its own
@@ -267,7 +273,8 @@ def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fuse
                       beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
                       window=wl.window, windows=windows, fused=fused, own_ranks=True,
-                      world=wl.world, arena=arena, min_gap=min_gap)
+                      world=wl.world, arena=arena, min_gap=min_gap,
+                      device_control=device_control)
     for k, i in enumerate(owned):
         a, b = packed[k], packed[k + 1]
         g0 = int(offs[i])
@@ -315,19 +322,20 @@ def main():
     if args.round_robin_owner is not None:
         shard, count_rr, n_owned, imbalance = build_round_robin(
             wl, args.round_robin_owner, arena=not args.no_arena,
-            min_gap=int(args.min_gap_gib * 2 ** 30), fused=not args.unfused)
+            min_gap=int(args.min_gap_gib * 2 ** 30), fused=not args.unfused,
+            device_control=args.graph)
         begin, end, padded, in_place = 0, count_rr, 0, False
         rr_info = {"owner": args.round_robin_owner, "owned_tensors": n_owned,
                    "owned_elems": count_rr, "largest_over_mean_owner": round(imbalance, 4)}
     elif args.workload == "buckets":
         shard, copy_in, padded, write_back = build_buckets(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
-            fused=not args.unfused, write_back=args.write_back)
+            fused=not args.unfused, write_back=args.write_back, device_control=args.graph)
         begin, end, in_place = 0, padded, False
     else:
         shard, begin, end, padded, in_place = build_shard(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
-            fused=not args.unfused)
+            fused=not args.unfused, device_control=args.graph)
     count = end - begin
     bufs = shard.rank_bufs
 
@@ -351,6 +359,15 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     applied = 0
     infos = []
+    graph = None
+    if args.graph:
+        # one captured step (copy-in, reduce+check windows, AdamW per owner,
+        # control update, write-back), replayed: per-step events bracket each
+        # replay, phases inside the graph are not separated
+        shard.sync_control()
+        t_before = shard.t
+        graph = shard.capture(bufs, before=copy_in, after=write_back)
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
@@ -358,6 +375,11 @@ def main():
     start.record()
     for k in range(args.steps):
         Z.zero_partition_layout(wl.numels, wl.world, wl.align)
+        if graph is not None:
+            ev[k][0].record()
+            graph.replay()
+            ev[k][3].record()
+            continue
         ev[k][4].record()
         if copy_in:
             copy_in()
@@ -368,8 +390,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
+    if graph is not None:
+        shard.sync_control()
+        applied = shard.t - t_before
+        r = Z.read_result(shard.res)
+        infos.append(type("Info", (), {"sumsq": r.sumsq})())
 
-    if args.unfused:
+    if graph is not None:
+        ms = {"step_graph": [e[0].elapsed_time(e[3]) for e in ev]}
+        bytes_per = {"step_graph": 2 * wl.world + 30 + (2 if args.unfused else 0)
+                     + (4 if copy_in else 0) + (4 if write_back else 0)}
+    elif args.unfused:
         ms = {"reduce": [], "check": [], "adamw": []}
         for e in ev:
             ms["reduce"].append(e[0].elapsed_time(e[1]))
@@ -382,10 +413,10 @@ def main():
             ms["reduce_check"].append(e[0].elapsed_time(e[2]))
             ms["adamw"].append(e[2].elapsed_time(e[3]))
         bytes_per = {"reduce_check": 2 * wl.world + 2, "adamw": 28}
-    if copy_in:
+    if copy_in and graph is None:
         ms["copy_in"] = [e[4].elapsed_time(e[0]) for e in ev]
         bytes_per["copy_in"] = 4
-    if write_back:
+    if write_back and graph is None:
         ms["write_back"] = [e[3].elapsed_time(e[5]) for e in ev]
         bytes_per["write_back"] = 4
     phases = {}
@@ -395,9 +426,21 @@ def main():
                      "GBps": round(bytes_per[k] * count / (avg * 1e-3) / 1e9, 1)}
     step_ms = total_ms / args.steps
     step_bytes = sum(bytes_per.values()) * count
-    adam_avg_s = float(np.mean(ms["adamw"])) * 1e-3
-    achieved = 28 * count / adam_avg_s / 1e9
-    traffic = measured_traffic("adamw_kernel", args.workload)
+    roofline = None
+    if "adamw" in ms:
+        adam_avg_s = float(np.mean(ms["adamw"])) * 1e-3
+        achieved = 28 * count / adam_avg_s / 1e9
+        roofline = {
+            "bound": "hbm",
+            "kernel": "adamw_kernel (zero_adamw_step)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("adamw_kernel", args.workload),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
+                            "factors from a known-size elementwise kernel)",
+        }
 
     result = {
         "metric": "params updated/s per GPU (ZeRO shard AdamW step) + achieved HBM GB/s % of peak",
@@ -426,6 +469,7 @@ def main():
             "clip": wl.clip,
             "in_place_reduce": in_place,
             "fused_reduce_check": not args.unfused,
+            "graph": bool(args.graph),
             "placement": ("separate allocations" if args.no_arena else
                           f"one arena, AdamW streams interleaved with rank buffers, "
                           f"min gap {args.min_gap_gib:g} GiB"),
@@ -437,17 +481,7 @@ def main():
         "applied_steps": applied,
         "final_norm": float(np.sqrt(infos[-1].sumsq)) if infos else None,
         "host_wall_s": round(wall, 4),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "adamw_kernel (zero_adamw_step)",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
-                            "factors from a known-size elementwise kernel)",
-        },
+        "roofline": roofline,
     }
     del bufs, shard
     torch.cuda.empty_cache()

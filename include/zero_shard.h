@@ -18,7 +18,11 @@
  *   4. adamw    AdamW on the partition's fp32 master weights, m and v, then the
  *               16-bit copy of the new weights (ZeRO-2 source walkthrough,
  *               sections 4.1 step 3 and 4.3);
- *   5. scaler   dynamic loss-scale update (wmrh.cn article, section 3.1).
+ *   5. scaler   dynamic loss-scale update (wmrh.cn article, section 3.1), on the
+ *               host (zero_loss_scaler_update) or on the device
+ *               (zero_step_control_update, with the *_ctl variants of 3 and 4
+ *               reading their per-step scalars from device memory so that a
+ *               step can be captured once in a HIP graph and replayed).
  *
  * Conventions for every call:
  *   - Buffers are flat arrays.  "device" pointers are HIP device memory owned
@@ -94,6 +98,29 @@ typedef struct zero_loss_scaler {
     int64_t skipped;    /* total steps skipped for overflow               */
 } zero_loss_scaler;
 
+/* Device-resident step control: the dynamic loss scaler of zero_loss_scaler
+ * and the AdamW step count, kept in device memory and advanced on the device
+ * (zero_step_control_update), so that a loop of owner steps needs no host
+ * round trip -- for example one step captured in a HIP graph and replayed.
+ * Filled on the host by zero_step_control_init, copied to the device by the
+ * caller, then only read by the *_ctl calls and advanced by
+ * zero_step_control_update.  The rules are those of zero_loss_scaler_update
+ * and zero_adamw_step (wmrh.cn article section 3.1: dynamic loss scaling,
+ * AdamW betas).  72 bytes, 8-byte aligned. */
+typedef struct zero_step_control {
+    double scale;       /* loss scale S of the next step                        */
+    double min_scale;   /* S never drops below this                             */
+    int64_t window;     /* clean steps in a row before S doubles                */
+    int64_t clean;      /* clean steps since the last change                    */
+    int64_t skipped;    /* steps skipped for overflow                           */
+    int64_t t;          /* AdamW steps applied so far                           */
+    float divisor;      /* D: gradients are unscaled by 1 / (S * D)             */
+    float inv_scale;    /* fp32(1 / (S * D)), the next step's unscale factor    */
+    float beta1, beta2; /* AdamW betas                                          */
+    float bc1, bc2;     /* fp32(1 - beta1^(t+1)), fp32(1 - beta2^(t+1)): the
+                           next applied step's bias corrections                 */
+} zero_step_control;
+
 /* One tensor of a flattened group (device array of these, sorted by offset,
  * for zero_flat_gather / zero_flat_scatter).  32 bytes. */
 typedef struct zero_tensor_desc {
@@ -148,6 +175,14 @@ int zero_memory_bytes(int32_t stage, int64_t numel_total, int64_t padded_total, 
  * clean += 1 and, when clean reaches window, S = 2S and clean = 0.
  * Errors: ZERO_EINVAL for a NULL state or window < 1. */
 int zero_loss_scaler_update(zero_loss_scaler* scaler, uint32_t overflow);
+
+/* Initial device step control (host struct, to be copied to device memory):
+ * S = scale0, t = 0, no clean or skipped steps; inv_scale, bc1 and bc2 for
+ * the first step (bc = 1 - beta, computed in fp64 and rounded once).
+ * Errors: ZERO_EINVAL for a NULL output, scale0 or min_scale not finite and
+ * > 0, window < 1, divisor not finite and > 0, or a beta outside [0, 1). */
+int zero_step_control_init(zero_step_control* ctl, double scale0, double min_scale,
+                           int64_t window, float divisor, float beta1, float beta2);
 
 /* Text for a status code (static storage). */
 const char* zero_status_str(int status);
@@ -272,6 +307,38 @@ int zero_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, void* para
                     const void* grad16, int64_t count, int32_t dtype,
                     const zero_adamw_hparams* hp, const zero_step_result* res,
                     hipStream_t stream);
+
+/* ------------------------------------- device-resident step control ---- */
+/* The same operations with the per-step scalars read from a device
+ * zero_step_control instead of host arguments, so that a whole step can be
+ * enqueued (or captured in a graph) once and replayed: the unscale factor is
+ * ctl->inv_scale, AdamW's betas and bias corrections are ctl->beta1/2 and
+ * ctl->bc1/2 (hp supplies lr, eps, weight_decay and max_grad_norm; hp->step
+ * is ignored).  ctl is device memory, read only by these calls. */
+int zero_reduce_check_owned_ctl(void* dst, const void* const* srcs, int32_t n_ranks,
+                                int64_t count, int32_t dtype, const zero_step_control* ctl,
+                                zero_step_result* res, void* workspace, size_t workspace_bytes,
+                                int32_t accumulate, hipStream_t stream);
+
+int zero_unscale_check_norm_ctl(const void* grad16, int64_t count, int32_t dtype,
+                                const zero_step_control* ctl, zero_step_result* res,
+                                void* workspace, size_t workspace_bytes, int32_t accumulate,
+                                hipStream_t stream);
+
+int zero_adamw_step_ctl(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
+                        const void* grad16, int64_t count, int32_t dtype,
+                        const zero_adamw_hparams* hp, const zero_step_control* ctl,
+                        const zero_step_result* res, hipStream_t stream);
+
+/* Ends a step on the device (one small kernel): with res->overflow set,
+ * S = max(S/2, min_scale), clean = 0, skipped += 1; otherwise t += 1,
+ * clean += 1 and, when clean reaches window, S = 2S and clean = 0.  Then
+ * inv_scale = fp32(1 / (S * D)) and bc1, bc2 for step t + 1 (fp64, rounded
+ * once).  Enqueue it after the step's last zero_adamw_step_ctl.
+ *   ctl  device, in/out;  res  device, in
+ * Errors: ZERO_EINVAL for NULL pointers. */
+int zero_step_control_update(zero_step_control* ctl, const zero_step_result* res,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

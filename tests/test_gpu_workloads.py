@@ -49,14 +49,15 @@ def _setup(wl, owner_ids, round_robin=False):
     return offs, padded, owners, begin, end, windows
 
 
-def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=False):
+def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=False,
+               device_control=False):
     wl = W.WORKLOADS[name]
     steps = wl.steps if steps is None else steps
     offs, padded, owners, begin, end, windows = _setup(wl, owner_ids, round_robin)
     shard = ShardStep(begin, end, owners, wl.dtype, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
                       eps=wl.eps, weight_decay=wl.weight_decay, max_grad_norm=wl.clip,
                       scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window, windows=windows,
-                      fused=fused)
+                      fused=fused, device_control=device_control)
     # initial state: device generator on the GPU, host generator for the oracle
     d_p16 = I.device_param16(wl, offs, begin, end)
     h_p16 = I.host_param16(wl, offs, begin, end, threads)
@@ -136,3 +137,20 @@ def test_buckets_small_all_owners_dynamic_scaling(fused):
     shard, scaler, skipped, t = run_parity("buckets_small", list(range(16)), fused=fused)
     # ten inf/NaN injections in 40 steps: ten halvings of 2^16, t = 30
     assert skipped == 10 and t == 30 and scaler.scale == 64.0
+
+
+@pytest.mark.parametrize("name,owners,fused", [("buckets_small", list(range(16)), True),
+                                               ("buckets_small", list(range(16)), False),
+                                               ("bert", [0], True)])
+def test_device_step_control(name, owners, fused):
+    """The loss scaler and the step count on the device (zero_step_control):
+    the *_ctl calls read the unscale factor, betas and bias corrections there
+    and zero_step_control_update advances them; every step matches the oracle
+    as the host-driven step does (scale, skips and t read back from the
+    device)."""
+    shard, scaler, skipped, t = run_parity(name, owners, fused=fused, device_control=True)
+    if name == "buckets_small":
+        assert skipped == 10 and t == 30 and scaler.scale == 64.0
+    c = Z.read_control(shard.ctl)
+    assert (c.scale, c.skipped, c.t) == (scaler.scale, scaler.skipped, t)
+

@@ -41,13 +41,25 @@ class zero_loss_scaler(ctypes.Structure):
                 ("skipped", ctypes.c_int64)]
 
 
+class zero_step_control(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_double), ("min_scale", ctypes.c_double),
+                ("window", ctypes.c_int64), ("clean", ctypes.c_int64),
+                ("skipped", ctypes.c_int64), ("t", ctypes.c_int64),
+                ("divisor", ctypes.c_float), ("inv_scale", ctypes.c_float),
+                ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("bc1", ctypes.c_float), ("bc2", ctypes.c_float)]
+
+
 RESULT_BYTES = ctypes.sizeof(zero_step_result)   # 16
+CONTROL_BYTES = ctypes.sizeof(zero_step_control)  # 72
 
 EXPORTS = (
     "zero_partition_layout", "zero_bucket_layout", "zero_memory_bytes",
     "zero_loss_scaler_update", "zero_status_str", "zero_init_master", "zero_reduce_owned",
     "zero_check_workspace_bytes", "zero_unscale_check_norm", "zero_reduce_check_owned",
     "zero_adamw_step", "zero_flat_gather", "zero_flat_scatter",
+    "zero_step_control_init", "zero_reduce_check_owned_ctl", "zero_unscale_check_norm_ctl",
+    "zero_adamw_step_ctl", "zero_step_control_update",
 )
 
 
@@ -90,6 +102,14 @@ def _load():
         "zero_adamw_step": ([P, P, P, P, P, i64, i32, P, P, P], ctypes.c_int),
         "zero_flat_gather": ([P, i64, P, i64, P], ctypes.c_int),
         "zero_flat_scatter": ([P, i64, P, i64, P], ctypes.c_int),
+        "zero_step_control_init": ([P, ctypes.c_double, ctypes.c_double, i64, f32, f32, f32],
+                                   ctypes.c_int),
+        "zero_reduce_check_owned_ctl": ([P, P, i32, i64, i32, P, P, P, ctypes.c_size_t, i32, P],
+                                        ctypes.c_int),
+        "zero_unscale_check_norm_ctl": ([P, i64, i32, P, P, P, ctypes.c_size_t, i32, P],
+                                        ctypes.c_int),
+        "zero_adamw_step_ctl": ([P, P, P, P, P, i64, i32, P, P, P, P], ctypes.c_int),
+        "zero_step_control_update": ([P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -281,6 +301,105 @@ def zero_flat_scatter(flat, descs, count: Optional[int] = None, stream=None) -> 
     _check(_lib.zero_flat_scatter(_dev(flat, 2, count, "flat"), count,
                                   descs.data_ptr() if descs.numel() else None, descs.shape[0],
                                   _stream(stream)), "zero_flat_scatter")
+
+
+# ------------------------------------------------ device step control -------
+def zero_step_control_init(scale0: float, min_scale: float = 1.0, window: int = 1000,
+                           divisor: float = 1.0, beta1: float = 0.9,
+                           beta2: float = 0.999) -> zero_step_control:
+    """Host zero_step_control for the first step (copy it to the device with
+    control_to_device)."""
+    c = zero_step_control()
+    _check(_lib.zero_step_control_init(ctypes.byref(c), float(scale0), float(min_scale),
+                                       int(window), float(divisor), float(beta1), float(beta2)),
+           "zero_step_control_init")
+    return c
+
+
+def control_to_device(ctl: zero_step_control, out=None, device="cuda"):
+    """A device tensor (uint8, 72 bytes, 256-byte aligned by the allocator)
+    holding `ctl`; written into `out` when given."""
+    import torch
+    host = torch.frombuffer(bytearray(bytes(ctl)), dtype=torch.uint8)
+    if out is None:
+        return host.to(device)
+    out.copy_(host)
+    return out
+
+
+def read_control(ctl_dev) -> zero_step_control:
+    """Copy a device zero_step_control to the host (synchronises the stream)."""
+    raw = ctl_dev.detach().cpu().numpy().tobytes()[:CONTROL_BYTES]
+    return zero_step_control.from_buffer_copy(raw)
+
+
+def _ctl(ctl_dev) -> int:
+    if not ctl_dev.is_cuda or ctl_dev.numel() * ctl_dev.element_size() < CONTROL_BYTES:
+        raise ValueError("ctl must be a device tensor of at least 72 bytes")
+    if ctl_dev.data_ptr() % 8:
+        raise ValueError("ctl must be 8-byte aligned")
+    return ctl_dev.data_ptr()
+
+
+def zero_reduce_check_owned_ctl(dst, srcs: Sequence, ctl_dev, res, workspace,
+                                accumulate: bool = False, count: Optional[int] = None,
+                                stream=None) -> None:
+    count = dst.numel() if count is None else count
+    dt = _dtype_code(dst)
+    if not 1 <= len(srcs) <= ZERO_MAX_RANKS:
+        raise ValueError("1..16 rank buffers")
+    for s in srcs:
+        if _dtype_code(s) != dt:
+            raise TypeError("rank buffers and dst must share the 16-bit type")
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    ptrs = (ctypes.c_void_p * len(srcs))(*[_dev(s, 2, count, "src") for s in srcs])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.zero_reduce_check_owned_ctl(_dev(dst, 2, count, "dst"), ptrs, len(srcs), count, dt,
+                                            _ctl(ctl_dev), res.data_ptr(),
+                                            _dev(workspace, workspace.element_size(), 0,
+                                                 "workspace"),
+                                            ws_bytes, int(bool(accumulate)), _stream(stream)),
+           "zero_reduce_check_owned_ctl")
+
+
+def zero_unscale_check_norm_ctl(grad16, ctl_dev, res, workspace, accumulate: bool = False,
+                                count: Optional[int] = None, stream=None) -> None:
+    count = grad16.numel() if count is None else count
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    _check(_lib.zero_unscale_check_norm_ctl(_dev(grad16, 2, count, "grad16"), count,
+                                            _dtype_code(grad16), _ctl(ctl_dev), res.data_ptr(),
+                                            _dev(workspace, workspace.element_size(), 0,
+                                                 "workspace"),
+                                            ws_bytes, int(bool(accumulate)), _stream(stream)),
+           "zero_unscale_check_norm_ctl")
+
+
+def zero_adamw_step_ctl(master, exp_avg, exp_avg_sq, param16, grad16, hp: zero_adamw_hparams,
+                        ctl_dev, res, count: Optional[int] = None, stream=None) -> None:
+    count = master.numel() if count is None else count
+    dt = _dtype_code(grad16)
+    if _dtype_code(param16) != dt:
+        raise TypeError("param16 and grad16 must share the 16-bit type")
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    _check(_lib.zero_adamw_step_ctl(_dev(master, 4, count, "master"),
+                                    _dev(exp_avg, 4, count, "exp_avg"),
+                                    _dev(exp_avg_sq, 4, count, "exp_avg_sq"),
+                                    _dev(param16, 2, count, "param16"),
+                                    _dev(grad16, 2, count, "grad16"), count, dt,
+                                    ctypes.byref(hp), _ctl(ctl_dev), res.data_ptr(),
+                                    _stream(stream)),
+           "zero_adamw_step_ctl")
+
+
+def zero_step_control_update(ctl_dev, res, stream=None) -> None:
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    _check(_lib.zero_step_control_update(_ctl(ctl_dev), res.data_ptr(), _stream(stream)),
+           "zero_step_control_update")
 
 
 def read_result(res) -> zero_step_result:

@@ -159,6 +159,20 @@ inline int launch(void (*kernel)(KArgs...), int64_t grid, unsigned lds, hipStrea
     return err == hipSuccess ? ZERO_OK : ZERO_EDEVICE;
 }
 
+// A small launch of `grid` blocks of `threads` lanes, no dynamic LDS.
+template <typename... KArgs, typename... Args>
+inline int launch_n(void (*kernel)(KArgs...), int grid, int threads, hipStream_t stream,
+                    Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> packed(static_cast<KArgs>(args)...);
+    void* ptrs[sizeof...(KArgs)];
+    int i = 0;
+    std::apply([&](auto&... a) { ((ptrs[i++] = (void*)&a), ...); }, packed);
+    const hipError_t err = hipLaunchKernel((const void*)kernel, dim3((unsigned)grid),
+                                           dim3((unsigned)threads), ptrs, 0, stream);
+    return err == hipSuccess ? ZERO_OK : ZERO_EDEVICE;
+}
+
 // Runs a tile kernel over `blocks` blocks as launches of at most
 // kMaxLaunchBlocks, in order on one stream: go(piece, grid) launches one
 // piece, whose Split has blk0 set.

@@ -177,11 +177,12 @@ constexpr int reduce_blocks_per_cu(int nr) { return nr >= 16 ? 1 : (16 / nr > 8 
 // the same lane).
 template <int DT, int NR, bool CHECK>
 __global__ void __launch_bounds__(kThreads)
-reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, double* part_sum,
-              uint32_t* part_flag) {
+reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, const zero_step_control* ctl,
+              double* part_sum, uint32_t* part_flag) {
     double sq = 0.0;
     uint32_t bad = 0;
     const int64_t blk = block_id(s);
+    if (CHECK && ctl) inv = ctl->inv_scale;             // device-resident step control
     if (s.aligned) {
         if (lane_tile<kReduceTiles>(s, kReduceTiles - 1) < s.nvec) {   // every row in range
             u32x4 w[kReduceTiles][NR];
@@ -242,10 +243,11 @@ reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, double* part_sum,
 // ------------------------------------------------------------- check -------
 template <int DT>
 __global__ void __launch_bounds__(kThreads)
-check_kernel(const uint16_t* __restrict__ g, Split s, float inv, double* __restrict__ part_sum,
-             uint32_t* __restrict__ part_flag) {
+check_kernel(const uint16_t* __restrict__ g, Split s, float inv, const zero_step_control* ctl,
+             double* __restrict__ part_sum, uint32_t* __restrict__ part_flag) {
     double sq = 0.0;
     uint32_t bad = 0;
+    if (ctl) inv = ctl->inv_scale;                      // device-resident step control
     const int64_t i = lane_tile(s);
     if (s.aligned) {
         if (i < s.nvec) {
@@ -299,7 +301,8 @@ fold_kernel(const double* __restrict__ in_sum, const uint32_t* __restrict__ in_f
 // of one owner).
 __global__ void __launch_bounds__(kThreads)
 finalize_kernel(const double* __restrict__ in_sum, const uint32_t* __restrict__ in_flag, int64_t n,
-                float inv_scale, int accumulate, zero_step_result* res) {
+                float inv_scale, const zero_step_control* ctl, int accumulate,
+                zero_step_result* res) {
     double s = 0.0;
     uint32_t f = 0;
     for (int64_t j = threadIdx.x; j < n; j += kThreads) {
@@ -314,7 +317,7 @@ finalize_kernel(const double* __restrict__ in_sum, const uint32_t* __restrict__ 
         }
         res->sumsq = s;
         res->overflow = f;
-        res->inv_scale = inv_scale;
+        res->inv_scale = ctl ? ctl->inv_scale : inv_scale;
     }
 }
 
@@ -361,17 +364,33 @@ __device__ __forceinline__ float clip_coef(const AdamConsts& c, const zero_step_
     return coef;
 }
 
+// The step's constants: the host's, or with device step control the betas
+// and bias corrections from ctl (1 - beta is exact in fp64, rounded once).
+__device__ __forceinline__ AdamConsts step_consts(AdamConsts c, const zero_step_control* ctl) {
+    if (ctl) {
+        c.b1 = ctl->beta1;
+        c.omb1 = (float)(1.0 - (double)c.b1);
+        c.b2 = ctl->beta2;
+        c.omb2 = (float)(1.0 - (double)c.b2);
+        c.bc1 = ctl->bc1;
+        c.bc2 = ctl->bc2;
+    }
+    return c;
+}
+
 template <int DT>
 __global__ void __launch_bounds__(kThreads)
 adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restrict__ va,
-             uint16_t* __restrict__ p16, const uint16_t* __restrict__ g16, Split s, AdamConsts c,
-             const zero_step_result* __restrict__ res) {
+             uint16_t* __restrict__ p16, const uint16_t* __restrict__ g16, Split s, AdamConsts c0,
+             const zero_step_control* __restrict__ ctl, const zero_step_result* __restrict__ res) {
     if (res->overflow) return;                       // skipped step: write nothing
-    // The clip factor is computed after the tile's loads are issued, so its
-    // fp64 square root and division overlap the HBM latency (computed before
-    // the loads they cost ~3% of the kernel's time at 2 blocks per CU).
+    // The clip factor (and, with device step control, the step's constants)
+    // are read after the tile's loads are issued, so the fp64 square root and
+    // division overlap the HBM latency (computed before the loads they cost
+    // ~3% of the kernel's time at 2 blocks per CU).
     const int64_t i = lane_tile(s);
     if (!s.aligned) {
+        const AdamConsts c = step_consts(c0, ctl);
         const float inv = res->inv_scale, coef = clip_coef(c, res);
         for (int64_t e = i * kVec; e < (i + 1) * kVec && e < s.count; ++e)
             adam_one<DT>(c, inv, coef, master, ma, va, p16, g16, e);
@@ -383,6 +402,7 @@ adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restri
         const f32x4 p0 = load_f4(master + e), p1 = load_f4(master + e + 4);
         const f32x4 m0 = load_f4(ma + e), m1 = load_f4(ma + e + 4);
         const f32x4 v0 = load_f4(va + e), v1 = load_f4(va + e + 4);
+        const AdamConsts c = step_consts(c0, ctl);
         const float inv = res->inv_scale, coef = clip_coef(c, res);
         f32x4 po[2], mo[2], vo[2];
         uint16_t ph[kVec];
@@ -408,12 +428,39 @@ adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restri
         store_b128(p16 + e, pack8(ph));
     }
     if (block_id(s) == 0) {
+        const AdamConsts c = step_consts(c0, ctl);
         const float inv = res->inv_scale, coef = clip_coef(c, res);
         const int t = threadIdx.x;
         if (t < s.head) adam_one<DT>(c, inv, coef, master, ma, va, p16, g16, t);
         else if (t >= 64 && t < 64 + kVec && s.head + s.nvec * kVec + (t - 64) < s.count)
             adam_one<DT>(c, inv, coef, master, ma, va, p16, g16, s.head + s.nvec * kVec + (t - 64));
     }
+}
+
+// ------------------------------------------------- device step control ---
+// One thread ends a step: the loss-scale rule of zero_loss_scaler_update, t
+// advanced on applied steps, and the next step's derived scalars.
+__global__ void __launch_bounds__(64)
+control_update_kernel(zero_step_control* ctl, const zero_step_result* res) {
+    if (threadIdx.x != 0) return;
+    zero_step_control c = *ctl;
+    if (res->overflow) {
+        const double half = c.scale * 0.5;
+        c.scale = half > c.min_scale ? half : c.min_scale;
+        c.clean = 0;
+        c.skipped += 1;
+    } else {
+        c.t += 1;
+        c.clean += 1;
+        if (c.clean >= c.window) {
+            c.scale = c.scale * 2.0;
+            c.clean = 0;
+        }
+    }
+    c.inv_scale = (float)(1.0 / (c.scale * (double)c.divisor));
+    c.bc1 = (float)(1.0 - pow((double)c.beta1, (double)(c.t + 1)));
+    c.bc2 = (float)(1.0 - pow((double)c.beta2, (double)(c.t + 1)));
+    *ctl = c;
 }
 
 // --------------------------------------------------------------- host ------
@@ -453,8 +500,8 @@ unsigned stream_grid(int64_t items) {
 }
 
 // Folds the level-0 partials into *res: fold passes, then the finalize block.
-int fold_into(char* ws, const Levels& L, float inv_scale, int32_t accumulate, zero_step_result* res,
-              hipStream_t stream) {
+int fold_into(char* ws, const Levels& L, float inv_scale, const zero_step_control* ctl,
+              int32_t accumulate, zero_step_result* res, hipStream_t stream) {
     for (int l = 0; l + 1 < L.n; ++l) {
         const int rc = launch(fold_kernel, L.parts[l + 1], 0, stream, (const double*)(ws + L.sum_off[l]),
                               (const uint32_t*)(ws + L.flag_off[l]), L.parts[l],
@@ -463,19 +510,19 @@ int fold_into(char* ws, const Levels& L, float inv_scale, int32_t accumulate, ze
     }
     const int last = L.n - 1;
     return launch(finalize_kernel, 1, 0, stream, (const double*)(ws + L.sum_off[last]),
-                  (const uint32_t*)(ws + L.flag_off[last]), L.parts[last], inv_scale,
+                  (const uint32_t*)(ws + L.flag_off[last]), L.parts[last], inv_scale, ctl,
                   (int)(accumulate != 0), res);
 }
 
 template <int DT, bool CHECK>
 int launch_reduce_n(uint16_t* dst, const RankPtrs& src, int n, const Split& s, float inv,
-                    double* ps, uint32_t* pf, hipStream_t stream) {
+                    const zero_step_control* ctl, double* ps, uint32_t* pf, hipStream_t stream) {
     const int64_t blocks = tile_blocks(s, kReduceTiles);
 #define ZERO_REDUCE_CASE(K)                                                                    \
     case K:                                                                                    \
         return launch_pieces(s, blocks, [&](const Split& piece, int64_t g) {                   \
             return launch(reduce_kernel<DT, K, CHECK>, g, lds_for_blocks(reduce_blocks_per_cu(K)), \
-                          stream, dst, src, piece, inv, ps, pf);                               \
+                          stream, dst, src, piece, inv, ctl, ps, pf);                          \
         });
     switch (n) {
         ZERO_REDUCE_CASE(1) ZERO_REDUCE_CASE(2) ZERO_REDUCE_CASE(3) ZERO_REDUCE_CASE(4)
@@ -511,6 +558,95 @@ int check_args(zero_step_result* res, void* workspace, size_t workspace_bytes, i
     if (!(inv_scale > 0.0f) || !__builtin_isfinite(inv_scale)) return ZERO_EINVAL;
     if (workspace_bytes < zero_check_workspace_bytes(count)) return ZERO_EINVAL;
     return ZERO_OK;
+}
+
+// Check and fused reduce+check; the unscale factor is inv_scale, or read on
+// the device from ctl when ctl is not null.
+int check_impl(const void* grad16, int64_t count, int32_t dtype, float inv_scale,
+               const zero_step_control* ctl, zero_step_result* res, void* workspace,
+               size_t workspace_bytes, int32_t accumulate, hipStream_t stream) {
+    if (count < 0 || !valid_dtype(dtype)) return ZERO_EINVAL;
+    if (count > 0 && !grad16) return ZERO_EINVAL;
+    int rc = check_args(res, workspace, workspace_bytes, count, inv_scale);
+    if (rc != ZERO_OK) return rc;
+    const void* p = grad16;
+    const Split s = split_for(vector_head(&p, 1, nullptr, 0), count);
+    const int64_t blocks = tile_blocks(s);
+    const Levels L = levels_for(blocks);
+    char* ws = (char*)workspace;
+    double* ps = (double*)(ws + L.sum_off[0]);
+    uint32_t* pf = (uint32_t*)(ws + L.flag_off[0]);
+    const uint16_t* g = (const uint16_t*)grad16;
+    rc = launch_pieces(s, blocks, [&](const Split& piece, int64_t grid) {
+        return dtype == ZERO_FP16
+                   ? launch(check_kernel<ZERO_FP16>, grid, 0, stream, g, piece, inv_scale, ctl,
+                            ps, pf)
+                   : launch(check_kernel<ZERO_BF16>, grid, 0, stream, g, piece, inv_scale, ctl,
+                            ps, pf);
+    });
+    if (rc != ZERO_OK) return rc;
+    return fold_into(ws, L, inv_scale, ctl, accumulate, res, stream);
+}
+
+int reduce_check_impl(void* dst, const void* const* srcs, int32_t n_ranks, int64_t count,
+                      int32_t dtype, float inv_scale, const zero_step_control* ctl,
+                      zero_step_result* res, void* workspace, size_t workspace_bytes,
+                      int32_t accumulate, hipStream_t stream) {
+    RankPtrs rp;
+    Split s;
+    int rc = reduce_args(dst, srcs, n_ranks, count, dtype, &rp, &s);
+    if (rc != ZERO_OK) return rc;
+    rc = check_args(res, workspace, workspace_bytes, count, inv_scale);
+    if (rc != ZERO_OK) return rc;
+    const int64_t blocks = tile_blocks(s, kReduceTiles);
+    const Levels L = levels_for(blocks);
+    char* ws = (char*)workspace;
+    double* ps = (double*)(ws + L.sum_off[0]);
+    uint32_t* pf = (uint32_t*)(ws + L.flag_off[0]);
+    uint16_t* d = (uint16_t*)dst;
+    rc = dtype == ZERO_FP16
+             ? launch_reduce_n<ZERO_FP16, true>(d, rp, n_ranks, s, inv_scale, ctl, ps, pf, stream)
+             : launch_reduce_n<ZERO_BF16, true>(d, rp, n_ranks, s, inv_scale, ctl, ps, pf, stream);
+    if (rc != ZERO_OK) return rc;
+    return fold_into(ws, L, inv_scale, ctl, accumulate, res, stream);
+}
+
+// AdamW over one partition; the step's betas and bias corrections come from
+// hp (hp->step) or, when ctl is not null, from ctl on the device.
+int adamw_impl(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
+               const void* grad16, int64_t count, int32_t dtype, const zero_adamw_hparams* hp,
+               const zero_step_control* ctl, const zero_step_result* res, hipStream_t stream) {
+    if (count < 0 || !valid_dtype(dtype) || !res) return ZERO_EINVAL;
+    if (count == 0) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !param16 || !grad16) return ZERO_EINVAL;
+    AdamConsts c;
+    const double t = ctl ? 1.0 : (double)hp->step;
+    c.decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
+    c.b1 = hp->beta1;
+    c.omb1 = (float)(1.0 - (double)hp->beta1);
+    c.b2 = hp->beta2;
+    c.omb2 = (float)(1.0 - (double)hp->beta2);
+    c.bc1 = (float)(1.0 - pow((double)hp->beta1, t));
+    c.bc2 = (float)(1.0 - pow((double)hp->beta2, t));
+    c.lr = hp->lr;
+    c.eps = hp->eps;
+    c.max_norm = hp->max_grad_norm;
+    const void* p16s[2] = {param16, grad16};
+    const void* p32s[3] = {master, exp_avg, exp_avg_sq};
+    const Split s = split_for(vector_head(p16s, 2, p32s, 3), count);
+    const int64_t blocks = tile_blocks(s);
+    uint16_t* p16 = (uint16_t*)param16;
+    const uint16_t* g16 = (const uint16_t*)grad16;
+    // 2 resident blocks per CU: 6.10 -> 6.37 TB/s on the LLaMA-70B-shaped
+    // shard, 5.33 -> 5.84 TB/s on the 7B one (MI355X)
+    const unsigned lds = lds_for_blocks(2);
+    return launch_pieces(s, blocks, [&](const Split& piece, int64_t grid) {
+        return dtype == ZERO_FP16
+                   ? launch(adamw_kernel<ZERO_FP16>, grid, lds, stream, master, exp_avg,
+                            exp_avg_sq, p16, g16, piece, c, ctl, res)
+                   : launch(adamw_kernel<ZERO_BF16>, grid, lds, stream, master, exp_avg,
+                            exp_avg_sq, p16, g16, piece, c, ctl, res);
+    });
 }
 
 }  // namespace
@@ -633,8 +769,10 @@ int zero_reduce_owned(void* dst, const void* const* srcs, int32_t n_ranks, int64
     if (rc != ZERO_OK || count == 0) return rc;
     uint16_t* d = (uint16_t*)dst;
     return dtype == ZERO_FP16
-               ? launch_reduce_n<ZERO_FP16, false>(d, rp, n_ranks, s, 0.0f, nullptr, nullptr, stream)
-               : launch_reduce_n<ZERO_BF16, false>(d, rp, n_ranks, s, 0.0f, nullptr, nullptr, stream);
+               ? launch_reduce_n<ZERO_FP16, false>(d, rp, n_ranks, s, 0.0f, nullptr, nullptr,
+                                                   nullptr, stream)
+               : launch_reduce_n<ZERO_BF16, false>(d, rp, n_ranks, s, 0.0f, nullptr, nullptr,
+                                                   nullptr, stream);
 }
 
 size_t zero_check_workspace_bytes(int64_t count) {
@@ -645,84 +783,81 @@ size_t zero_check_workspace_bytes(int64_t count) {
 int zero_unscale_check_norm(const void* grad16, int64_t count, int32_t dtype, float inv_scale,
                             zero_step_result* res, void* workspace, size_t workspace_bytes,
                             int32_t accumulate, hipStream_t stream) {
-    if (count < 0 || !valid_dtype(dtype)) return ZERO_EINVAL;
-    if (count > 0 && !grad16) return ZERO_EINVAL;
-    int rc = check_args(res, workspace, workspace_bytes, count, inv_scale);
-    if (rc != ZERO_OK) return rc;
-    const void* p = grad16;
-    const Split s = split_for(vector_head(&p, 1, nullptr, 0), count);
-    const int64_t blocks = tile_blocks(s);
-    const Levels L = levels_for(blocks);
-    char* ws = (char*)workspace;
-    double* ps = (double*)(ws + L.sum_off[0]);
-    uint32_t* pf = (uint32_t*)(ws + L.flag_off[0]);
-    const uint16_t* g = (const uint16_t*)grad16;
-    rc = launch_pieces(s, blocks, [&](const Split& piece, int64_t grid) {
-        return dtype == ZERO_FP16
-                   ? launch(check_kernel<ZERO_FP16>, grid, 0, stream, g, piece, inv_scale, ps, pf)
-                   : launch(check_kernel<ZERO_BF16>, grid, 0, stream, g, piece, inv_scale, ps, pf);
-    });
-    if (rc != ZERO_OK) return rc;
-    return fold_into(ws, L, inv_scale, accumulate, res, stream);
+    return check_impl(grad16, count, dtype, inv_scale, nullptr, res, workspace, workspace_bytes,
+                      accumulate, stream);
+}
+
+int zero_unscale_check_norm_ctl(const void* grad16, int64_t count, int32_t dtype,
+                                const zero_step_control* ctl, zero_step_result* res,
+                                void* workspace, size_t workspace_bytes, int32_t accumulate,
+                                hipStream_t stream) {
+    if (!ctl) return ZERO_EINVAL;
+    return check_impl(grad16, count, dtype, 1.0f, ctl, res, workspace, workspace_bytes,
+                      accumulate, stream);
 }
 
 int zero_reduce_check_owned(void* dst, const void* const* srcs, int32_t n_ranks, int64_t count,
                             int32_t dtype, float inv_scale, zero_step_result* res, void* workspace,
                             size_t workspace_bytes, int32_t accumulate, hipStream_t stream) {
-    RankPtrs rp;
-    Split s;
-    int rc = reduce_args(dst, srcs, n_ranks, count, dtype, &rp, &s);
-    if (rc != ZERO_OK) return rc;
-    rc = check_args(res, workspace, workspace_bytes, count, inv_scale);
-    if (rc != ZERO_OK) return rc;
-    const int64_t blocks = tile_blocks(s, kReduceTiles);
-    const Levels L = levels_for(blocks);
-    char* ws = (char*)workspace;
-    double* ps = (double*)(ws + L.sum_off[0]);
-    uint32_t* pf = (uint32_t*)(ws + L.flag_off[0]);
-    uint16_t* d = (uint16_t*)dst;
-    rc = dtype == ZERO_FP16
-             ? launch_reduce_n<ZERO_FP16, true>(d, rp, n_ranks, s, inv_scale, ps, pf, stream)
-             : launch_reduce_n<ZERO_BF16, true>(d, rp, n_ranks, s, inv_scale, ps, pf, stream);
-    if (rc != ZERO_OK) return rc;
-    return fold_into(ws, L, inv_scale, accumulate, res, stream);
+    return reduce_check_impl(dst, srcs, n_ranks, count, dtype, inv_scale, nullptr, res, workspace,
+                             workspace_bytes, accumulate, stream);
+}
+
+int zero_reduce_check_owned_ctl(void* dst, const void* const* srcs, int32_t n_ranks,
+                                int64_t count, int32_t dtype, const zero_step_control* ctl,
+                                zero_step_result* res, void* workspace, size_t workspace_bytes,
+                                int32_t accumulate, hipStream_t stream) {
+    if (!ctl) return ZERO_EINVAL;
+    return reduce_check_impl(dst, srcs, n_ranks, count, dtype, 1.0f, ctl, res, workspace,
+                             workspace_bytes, accumulate, stream);
 }
 
 int zero_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
                     const void* grad16, int64_t count, int32_t dtype,
                     const zero_adamw_hparams* hp, const zero_step_result* res,
                     hipStream_t stream) {
-    if (count < 0 || !valid_dtype(dtype) || !hp || !res || hp->step < 1) return ZERO_EINVAL;
-    if (count == 0) return ZERO_OK;
-    if (!master || !exp_avg || !exp_avg_sq || !param16 || !grad16) return ZERO_EINVAL;
-    AdamConsts c;
-    const double t = (double)hp->step;
-    c.decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
-    c.b1 = hp->beta1;
-    c.omb1 = (float)(1.0 - (double)hp->beta1);
-    c.b2 = hp->beta2;
-    c.omb2 = (float)(1.0 - (double)hp->beta2);
-    c.bc1 = (float)(1.0 - pow((double)hp->beta1, t));
-    c.bc2 = (float)(1.0 - pow((double)hp->beta2, t));
-    c.lr = hp->lr;
-    c.eps = hp->eps;
-    c.max_norm = hp->max_grad_norm;
-    const void* p16s[2] = {param16, grad16};
-    const void* p32s[3] = {master, exp_avg, exp_avg_sq};
-    const Split s = split_for(vector_head(p16s, 2, p32s, 3), count);
-    const int64_t blocks = tile_blocks(s);
-    uint16_t* p16 = (uint16_t*)param16;
-    const uint16_t* g16 = (const uint16_t*)grad16;
-    // 2 resident blocks per CU: 6.10 -> 6.37 TB/s on the LLaMA-70B-shaped
-    // shard, 5.33 -> 5.84 TB/s on the 7B one (MI355X)
-    const unsigned lds = lds_for_blocks(2);
-    return launch_pieces(s, blocks, [&](const Split& piece, int64_t grid) {
-        return dtype == ZERO_FP16
-                   ? launch(adamw_kernel<ZERO_FP16>, grid, lds, stream, master, exp_avg,
-                            exp_avg_sq, p16, g16, piece, c, res)
-                   : launch(adamw_kernel<ZERO_BF16>, grid, lds, stream, master, exp_avg,
-                            exp_avg_sq, p16, g16, piece, c, res);
-    });
+    if (!hp || hp->step < 1) return ZERO_EINVAL;
+    return adamw_impl(master, exp_avg, exp_avg_sq, param16, grad16, count, dtype, hp, nullptr, res,
+                      stream);
+}
+
+int zero_adamw_step_ctl(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
+                        const void* grad16, int64_t count, int32_t dtype,
+                        const zero_adamw_hparams* hp, const zero_step_control* ctl,
+                        const zero_step_result* res, hipStream_t stream) {
+    if (!hp || !ctl) return ZERO_EINVAL;
+    return adamw_impl(master, exp_avg, exp_avg_sq, param16, grad16, count, dtype, hp, ctl, res,
+                      stream);
+}
+
+int zero_step_control_init(zero_step_control* ctl, double scale0, double min_scale,
+                           int64_t window, float divisor, float beta1, float beta2) {
+    if (!ctl || !(scale0 > 0.0) || !__builtin_isfinite(scale0) || !(min_scale > 0.0) ||
+        !__builtin_isfinite(min_scale) || window < 1 || !(divisor > 0.0f) ||
+        !__builtin_isfinite(divisor) || !(beta1 >= 0.0f && beta1 < 1.0f) ||
+        !(beta2 >= 0.0f && beta2 < 1.0f))
+        return ZERO_EINVAL;
+    zero_step_control c;
+    c.scale = scale0;
+    c.min_scale = min_scale;
+    c.window = window;
+    c.clean = 0;
+    c.skipped = 0;
+    c.t = 0;
+    c.divisor = divisor;
+    c.inv_scale = (float)(1.0 / (scale0 * (double)divisor));
+    c.beta1 = beta1;
+    c.beta2 = beta2;
+    c.bc1 = (float)(1.0 - pow((double)beta1, 1.0));
+    c.bc2 = (float)(1.0 - pow((double)beta2, 1.0));
+    *ctl = c;
+    return ZERO_OK;
+}
+
+int zero_step_control_update(zero_step_control* ctl, const zero_step_result* res,
+                             hipStream_t stream) {
+    if (!ctl || !res) return ZERO_EINVAL;
+    return launch_n(control_update_kernel, 1, 64, stream, ctl, res);
 }
 
 }  // extern "C"

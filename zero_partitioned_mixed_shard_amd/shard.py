@@ -15,6 +15,12 @@ runs one step as the library's calls:
 With fused=False the reduce and the check are separate calls
 (zero_reduce_owned per window, then zero_unscale_check_norm per owner).
 
+With device_control=True the loss scaler and the step count live on the
+device (zero_step_control): the step runs the *_ctl calls and ends with
+zero_step_control_update, so it needs no host round trip and can be
+captured once in a HIP graph (capture()) and replayed; finish() only reads
+the result and the control back for reporting.
+
 Placement.  With own_ranks=True the step also holds the N simulated rank
 buffers.  With arena=True every large buffer is carved from one device
 allocation in an order that keeps the arrays AdamW streams together (master,
@@ -34,10 +40,12 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-from . import (RESULT_BYTES, ZERO_BF16, ZERO_FP16, read_result, zero_adamw_hparams,
-               zero_adamw_step, zero_check_workspace_bytes, zero_init_master,
-               zero_loss_scaler, zero_loss_scaler_update, zero_reduce_check_owned,
-               zero_reduce_owned, zero_unscale_check_norm)
+from . import (RESULT_BYTES, ZERO_BF16, ZERO_FP16, control_to_device, read_control,
+               read_result, zero_adamw_hparams, zero_adamw_step, zero_adamw_step_ctl,
+               zero_check_workspace_bytes, zero_init_master, zero_loss_scaler,
+               zero_loss_scaler_update, zero_reduce_check_owned, zero_reduce_check_owned_ctl,
+               zero_reduce_owned, zero_step_control_init, zero_step_control_update,
+               zero_unscale_check_norm, zero_unscale_check_norm_ctl)
 
 
 @dataclass
@@ -57,7 +65,7 @@ class ShardStep:
                  scale0=1.0, min_scale=1.0, window=1000, windows: Optional[Sequence[Tuple[int, int]]] = None,
                  divisor: int = 1, in_place_rank: Optional[int] = None, fused: bool = True,
                  own_ranks: bool = False, world: int = 0, arena: bool = False,
-                 min_gap: int = 0, device="cuda"):
+                 min_gap: int = 0, device_control: bool = False, device="cuda"):
         self.begin, self.end = begin, end
         self.count = end - begin
         self.owners = [(a - begin, b - begin) for a, b in owners]
@@ -91,6 +99,10 @@ class ShardStep:
         self.exp_avg.zero_()
         self.exp_avg_sq.zero_()
         self.res = torch.zeros(RESULT_BYTES // 4, dtype=torch.int32, device=device)
+        self.ctl = None
+        if device_control:
+            self.ctl = control_to_device(zero_step_control_init(
+                scale0, min_scale, window, float(divisor), beta1, beta2), device=device)
         spans = [b - a for a, b in self.owners] + [b - a for a, b in self.reduce_ranges]
         ws = max(zero_check_workspace_bytes(n) for n in spans) if spans else 64
         self.workspace = torch.empty((ws + 7) // 8, dtype=torch.float64, device=device)
@@ -157,19 +169,26 @@ class ShardStep:
 
     def launch(self, rank_bufs: Optional[Sequence[torch.Tensor]] = None,
                marks: Optional[List] = None) -> None:
-        """Enqueue reduce -> check -> AdamW on the current stream.  `marks`
-        (4 events) are recorded before reduce, check, AdamW and after.
-        Without rank_bufs the step's own rank buffers are used."""
+        """Enqueue reduce -> check -> AdamW on the current stream (and, with
+        device control, the control update).  `marks` (4 events) are recorded
+        before reduce, check, AdamW and after.  Without rank_bufs the step's
+        own rank buffers are used."""
         if rank_bufs is None:
             rank_bufs = self.rank_bufs
         red = self.reduced(rank_bufs)
+        ctl = self.ctl
         inv = self.inv_scale
         if marks:
             marks[0].record()
         if self.fused:
             for k, (a, b) in enumerate(self.reduce_ranges):
-                zero_reduce_check_owned(red[a:b], [r[a:b] for r in rank_bufs], inv, self.res,
-                                        self.workspace, accumulate=k > 0)
+                srcs = [r[a:b] for r in rank_bufs]
+                if ctl is None:
+                    zero_reduce_check_owned(red[a:b], srcs, inv, self.res, self.workspace,
+                                            accumulate=k > 0)
+                else:
+                    zero_reduce_check_owned_ctl(red[a:b], srcs, ctl, self.res, self.workspace,
+                                                accumulate=k > 0)
             if marks:
                 marks[1].record()
         else:
@@ -178,25 +197,64 @@ class ShardStep:
             if marks:
                 marks[1].record()
             for k, (a, b) in enumerate(self.owners):
-                zero_unscale_check_norm(red[a:b], inv, self.res, self.workspace, accumulate=k > 0)
+                if ctl is None:
+                    zero_unscale_check_norm(red[a:b], inv, self.res, self.workspace,
+                                            accumulate=k > 0)
+                else:
+                    zero_unscale_check_norm_ctl(red[a:b], ctl, self.res, self.workspace,
+                                                accumulate=k > 0)
         if marks:
             marks[2].record()
         self.hp.step = self.t + 1
         for a, b in self.owners:
-            zero_adamw_step(self.master[a:b], self.exp_avg[a:b], self.exp_avg_sq[a:b],
-                            self.param16[a:b], red[a:b], self.hp, self.res)
+            args = (self.master[a:b], self.exp_avg[a:b], self.exp_avg_sq[a:b],
+                    self.param16[a:b], red[a:b], self.hp)
+            if ctl is None:
+                zero_adamw_step(*args, self.res)
+            else:
+                zero_adamw_step_ctl(*args, ctl, self.res)
+        if ctl is not None:
+            zero_step_control_update(ctl, self.res)
         if marks:
             marks[3].record()
 
     def finish(self) -> StepInfo:
-        """Read the 16-byte result (synchronises) and update t and the scaler."""
+        """Read the 16-byte result (synchronises) and update t and the scaler
+        (with device control: read them back from the device)."""
         r = read_result(self.res)
         used = self.scaler.scale
         applied = not r.overflow
-        if applied:
-            self.t += 1
-        zero_loss_scaler_update(self.scaler, r.overflow)
+        if self.ctl is not None:
+            self.sync_control()
+        else:
+            if applied:
+                self.t += 1
+            zero_loss_scaler_update(self.scaler, r.overflow)
         return StepInfo(int(r.overflow), float(r.sumsq), applied, used, self.t)
+
+    def sync_control(self) -> None:
+        """Host copies of the device control's scale, counters and t
+        (synchronises the stream)."""
+        c = read_control(self.ctl)
+        self.scaler.scale, self.scaler.clean, self.scaler.skipped = c.scale, c.clean, c.skipped
+        self.t = c.t
+
+    def capture(self, rank_bufs: Optional[Sequence[torch.Tensor]] = None,
+                before=None, after=None) -> "torch.cuda.CUDAGraph":
+        """One whole step (optionally preceded by before(), e.g. a copy-in,
+        and followed by after(), e.g. a write-back) captured in a HIP graph;
+        each replay runs the next step.  Needs device_control=True: every
+        per-step scalar is read on the device."""
+        if self.ctl is None:
+            raise ValueError("capture() needs device_control=True")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            if before is not None:
+                before()
+            self.launch(rank_bufs)
+            if after is not None:
+                after()
+        return g
 
     def step(self, rank_bufs: Optional[Sequence[torch.Tensor]] = None,
              marks: Optional[List] = None) -> StepInfo:
