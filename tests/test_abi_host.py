@@ -102,3 +102,26 @@ def test_status_strings():
         ws = Z.zero_check_workspace_bytes(n)
         assert 12 * (n // 2048) <= ws <= n / 170 + 1024
     assert Z.zero_check_workspace_bytes(8_622_081_024) < 51e6
+
+
+@pytest.mark.parametrize("scale0,divisor,betas", [(2.0 ** 16, 1.0, (0.9, 0.999)),
+                                                  (1.0, 8.0, (0.9, 0.95)),
+                                                  (3.0, 3.0, (0.0, 0.5))])
+def test_step_control_init_matches_oracle_constants(scale0, divisor, betas):
+    """The device step control's first-step scalars are the oracle's: the
+    unscale factor fp32(1/(S*D)) and AdamW's bias corrections for t = 1."""
+    import ctypes
+    c = Z.zero_step_control_init(scale0, 1.0, 1000, divisor, *betas)
+    assert (c.scale, c.min_scale, c.window, c.clean, c.skipped, c.t) == (scale0, 1.0, 1000, 0, 0, 0)
+    assert c.inv_scale == float(np.float32(1.0 / (scale0 * divisor)))
+    want = oracle.adam_consts(oracle.HParams(1e-3, betas[0], betas[1], 1e-8, 0.01, 0.0), 1)
+    assert (c.bc1, c.bc2) == (want["bc1"], want["bc2"])
+    assert (c.beta1, c.beta2) == (want["b1"], want["b2"])
+    assert ctypes.sizeof(c) == 72
+
+
+def test_step_control_init_errors():
+    for args in ((0.0,), (1.0, 0.0), (1.0, 1.0, 0), (1.0, 1.0, 10, 0.0), (1.0, 1.0, 10, 1.0, 1.0),
+                 (1.0, 1.0, 10, 1.0, 0.9, -0.1), (float("inf"),)):
+        with pytest.raises(Z.ZeroError):
+            Z.zero_step_control_init(*args)

@@ -406,3 +406,34 @@ def test_invalid_arguments_launch_nothing():
                              16, FP16, ctypes.byref(hp), res.data_ptr(), None) == Z.ZERO_EINVAL
     torch.cuda.synchronize()
     assert (dst == 0).all()
+
+
+def test_step_control_update_matches_host_rules():
+    """zero_step_control_update against the host loss scaler and the oracle's
+    constants over 300 steps with random overflow flags, a 3-step doubling
+    window and a floor: scale, counters and t exact; inv_scale exact; the
+    bias corrections for the next step equal the host's fp64 pow rounded to
+    fp32 (device pow: allowed 1 ulp, counted)."""
+    rng = np.random.default_rng(5)
+    ctl_h = Z.zero_step_control_init(64.0, 2.0, 3, 2.0, 0.9, 0.999)
+    ctl = Z.control_to_device(ctl_h)
+    scaler = Z.zero_loss_scaler(64.0, 2.0, 3, 0, 0)
+    t = 0
+    res = _res_tensor()
+    exact = 0
+    for k in range(300):
+        flag = int(rng.random() < 0.35)
+        res.zero_()
+        res[2] = flag                                     # zero_step_result.overflow
+        Z.zero_step_control_update(ctl, res)
+        c = Z.read_control(ctl)
+        Z.zero_loss_scaler_update(scaler, flag)
+        t += 1 - flag
+        assert (c.scale, c.clean, c.skipped, c.t) == (scaler.scale, scaler.clean, scaler.skipped, t)
+        assert c.inv_scale == float(np.float32(1.0 / (scaler.scale * 2.0)))
+        want = oracle.adam_consts(oracle.HParams(), t + 1)
+        for got, w in ((c.bc1, want["bc1"]), (c.bc2, want["bc2"])):
+            d = abs(int(np.float32(got).view(np.int32)) - int(np.float32(w).view(np.int32)))
+            assert d <= 1, (k, got, w)
+            exact += d == 0
+    print(f"bias corrections equal to the host's in {exact} of 600", flush=True)
