@@ -121,8 +121,8 @@ typedef struct zero_step_control {
                            next applied step's bias corrections                 */
 } zero_step_control;
 
-/* One tensor of a flattened group (device array of these, sorted by offset,
- * for zero_flat_gather / zero_flat_scatter).  32 bytes. */
+/* One tensor of a flattened group (device array of these in flat order, for
+ * zero_flat_gather / zero_flat_scatter).  32 bytes. */
 typedef struct zero_tensor_desc {
     void* ptr;          /* device pointer to the tensor's `numel` 16-bit values   */
     int64_t offset;     /* index of the tensor's first element in the flat buffer */
@@ -205,8 +205,11 @@ int zero_init_master(float* master, const void* param16, int64_t count, int32_t 
  *   every flat element in [0, flat_count) that no descriptor covers is set to 0
  *   (the alignment padding).
  *   flat[flat_count]   device, out, 16-bit patterns (copied unchanged)
- *   descs[n_descs]     device array, sorted by offset, ranges disjoint and
- *                      inside [0, flat_count); each ptr valid for numel values.
+ *   descs[n_descs]     device array in flat order: descs[k+1].offset >=
+ *                      descs[k].offset + descs[k].numel (a zero-size tensor
+ *                      may share the offset of the tensor after it), every
+ *                      range inside [0, flat_count); each ptr valid for numel
+ *                      values.
  * The kernel reads a tensor only at indices below its numel and writes the
  * flat buffer only below flat_count, so a table that breaks the ordering rule
  * gives wrong values but no out-of-range access.
