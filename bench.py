@@ -425,6 +425,11 @@ def main():
         phases[k] = {"ms": round(avg, 4), "bytes_per_elem": bytes_per[k],
                      "GBps": round(bytes_per[k] * count / (avg * 1e-3) / 1e9, 1)}
     step_ms = total_ms / args.steps
+    # each step's own device time: from its first event (copy-in or reduce)
+    # to its last (AdamW, or the write-back)
+    first = 0 if (graph is not None or not copy_in) else 4
+    last = 5 if (write_back and graph is None) else 3
+    per_step = [e[first].elapsed_time(e[last]) for e in ev]
     step_bytes = sum(bytes_per.values()) * count
     roofline = None
     if "adamw" in ms:
@@ -479,6 +484,8 @@ def main():
         "step_frac_of_peak": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "phases": phases,
         "applied_steps": applied,
+        "per_step_ms": [round(x, 4) for x in per_step],
+        "median_step_ms": round(float(np.median(per_step)), 4),
         "final_norm": float(np.sqrt(infos[-1].sumsq)) if infos else None,
         "host_wall_s": round(wall, 4),
         "roofline": roofline,
