@@ -125,3 +125,25 @@ def test_step_control_init_errors():
                  (1.0, 1.0, 10, 1.0, 0.9, -0.1), (float("inf"),)):
         with pytest.raises(Z.ZeroError):
             Z.zero_step_control_init(*args)
+
+
+def test_device_control_calls_reject_null_pointers_before_launching():
+    """Argument checks run on the host before anything is launched, so they
+    need no GPU: a NULL control block, result or buffer is ZERO_EINVAL."""
+    import ctypes
+    L = Z.lib()
+    hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    fake = ctypes.c_void_p(0x10000)          # never dereferenced: every call fails first
+    srcs = (ctypes.c_void_p * 1)(fake)
+    assert L.zero_step_control_update(None, fake, None) == Z.ZERO_EINVAL
+    assert L.zero_step_control_update(fake, None, None) == Z.ZERO_EINVAL
+    assert L.zero_reduce_check_owned_ctl(fake, srcs, 1, 16, Z.ZERO_BF16, None, fake, fake, 1 << 20,
+                                         0, None) == Z.ZERO_EINVAL
+    assert L.zero_unscale_check_norm_ctl(fake, 16, Z.ZERO_BF16, None, fake, fake, 1 << 20, 0,
+                                         None) == Z.ZERO_EINVAL
+    assert L.zero_adamw_step_ctl(fake, fake, fake, fake, fake, 16, Z.ZERO_BF16, ctypes.byref(hp),
+                                 None, fake, None) == Z.ZERO_EINVAL
+    assert L.zero_adamw_step_ctl(fake, fake, fake, fake, fake, 16, 7, ctypes.byref(hp), fake, fake,
+                                 None) == Z.ZERO_EINVAL
+    assert L.zero_adamw_step_ctl(fake, fake, fake, fake, fake, 16, Z.ZERO_BF16, None, fake, fake,
+                                 None) == Z.ZERO_EINVAL
