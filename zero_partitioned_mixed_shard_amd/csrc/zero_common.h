@@ -142,12 +142,12 @@ inline unsigned lds_for_blocks(int b) {
     return b >= 8 ? 0u : kLdsPerCU / (unsigned)(b + 1) + 2048u;
 }
 
-// Launches `kernel` on `grid` blocks with `lds` bytes of dynamic LDS, its
-// arguments converted to the kernel's parameter types, and returns this
-// launch's own status (not a stale thread-local one).
+// Launches `kernel` on `grid` blocks of `threads` lanes with `lds` bytes of
+// dynamic LDS, its arguments converted to the kernel's parameter types, and
+// returns this launch's own status (not a stale thread-local one).
 template <typename... KArgs, typename... Args>
-inline int launch(void (*kernel)(KArgs...), int64_t grid, unsigned lds, hipStream_t stream,
-                  Args... args) {
+inline int launch_shape(void (*kernel)(KArgs...), int64_t grid, int threads, unsigned lds,
+                        hipStream_t stream, Args... args) {
     static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
     if (grid < 1 || grid > kMaxLaunchBlocks) return ZERO_ERANGE;
     std::tuple<KArgs...> packed(static_cast<KArgs>(args)...);
@@ -155,22 +155,15 @@ inline int launch(void (*kernel)(KArgs...), int64_t grid, unsigned lds, hipStrea
     int i = 0;
     std::apply([&](auto&... a) { ((ptrs[i++] = (void*)&a), ...); }, packed);
     const hipError_t err = hipLaunchKernel((const void*)kernel, dim3((unsigned)grid),
-                                           dim3(kThreads), ptrs, lds, stream);
+                                           dim3((unsigned)threads), ptrs, lds, stream);
     return err == hipSuccess ? ZERO_OK : ZERO_EDEVICE;
 }
 
-// A small launch of `grid` blocks of `threads` lanes, no dynamic LDS.
+// A launch of 256-lane blocks (every kernel but the one-thread control update).
 template <typename... KArgs, typename... Args>
-inline int launch_n(void (*kernel)(KArgs...), int grid, int threads, hipStream_t stream,
-                    Args... args) {
-    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
-    std::tuple<KArgs...> packed(static_cast<KArgs>(args)...);
-    void* ptrs[sizeof...(KArgs)];
-    int i = 0;
-    std::apply([&](auto&... a) { ((ptrs[i++] = (void*)&a), ...); }, packed);
-    const hipError_t err = hipLaunchKernel((const void*)kernel, dim3((unsigned)grid),
-                                           dim3((unsigned)threads), ptrs, 0, stream);
-    return err == hipSuccess ? ZERO_OK : ZERO_EDEVICE;
+inline int launch(void (*kernel)(KArgs...), int64_t grid, unsigned lds, hipStream_t stream,
+                  Args... args) {
+    return launch_shape(kernel, grid, kThreads, lds, stream, args...);
 }
 
 // Runs a tile kernel over `blocks` blocks as launches of at most

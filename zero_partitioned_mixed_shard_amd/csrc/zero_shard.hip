@@ -857,7 +857,7 @@ int zero_step_control_init(zero_step_control* ctl, double scale0, double min_sca
 int zero_step_control_update(zero_step_control* ctl, const zero_step_result* res,
                              hipStream_t stream) {
     if (!ctl || !res) return ZERO_EINVAL;
-    return launch_n(control_update_kernel, 1, 64, stream, ctl, res);
+    return launch_shape(control_update_kernel, 1, 64, 0u, stream, ctl, res);
 }
 
 }  // extern "C"
