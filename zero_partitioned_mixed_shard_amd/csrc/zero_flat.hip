@@ -28,32 +28,6 @@ __device__ __forceinline__ int64_t desc_at(const zero_tensor_desc* d, int64_t n,
     return lo - 1;
 }
 
-// Index of the last descriptor whose offset is <= e, or -1, found by one
-// whole wave: each round tests 64 evenly spaced descriptors at once and keeps
-// the interval between the last one at or below e and the next, so a table
-// of n entries costs ceil(log64 n) dependent loads (a binary search by one
-// thread: log2 n; on a 3,300-tensor bucket 2 loads instead of 12, which
-// matters because every block waits for it).  Every lane of the wave calls
-// it with the same e.  Every index it reads lies in [0, n), whatever the
-// table holds.
-__device__ __forceinline__ int64_t wave_desc_at(const zero_tensor_desc* d, int64_t n, int64_t e) {
-    const int lane = threadIdx.x & 63;
-    int64_t lo = 0, hi = n;           // lo == 0 or d[lo].offset <= e; answer in [lo - 1, hi)
-    while (hi - lo > 64) {
-        const int64_t step = (hi - lo + 63) / 64;
-        const int64_t j = lo + (int64_t)lane * step;
-        const bool le = j < hi && d[j].offset <= e;
-        const int c = __popcll(__ballot(le));
-        if (c == 0) return lo - 1;    // only when lo == 0: e lies before every tensor
-        const int64_t nhi = lo + (int64_t)c * step;
-        lo = lo + (int64_t)(c - 1) * step;
-        hi = nhi < hi ? nhi : hi;
-    }
-    const int64_t j = lo + lane;
-    const bool le = j < hi && d[j].offset <= e;
-    return lo + __popcll(__ballot(le)) - 1;
-}
-
 // A lane's view of the descriptor table: the tensor holding the flat
 // elements it is at, advanced forward only.
 struct DescCursor {
@@ -149,16 +123,57 @@ __device__ __forceinline__ void store_elems(g_u16* p, u32x4 w, int first, int n)
 // once for 4 rows, and a lane has the loads of all 4 rows in flight at once.
 constexpr int kFlatRows = 4;
 
-// First descriptor at or below flat element e for the whole block (wave 0
-// searches, LDS broadcasts).  Every thread of the block calls it.
-__device__ __forceinline__ int64_t block_first_desc(const zero_tensor_desc* d, int64_t n, int64_t e) {
-    __shared__ int64_t s_first;
+// The block's cursor at flat element e: the last descriptor at or below e
+// and the next one's offset, found by wave 0 with a 64-wide search (each
+// round tests 64 evenly spaced descriptors at once) and broadcast through
+// LDS.  Every thread of the block calls it; every index it reads lies in
+// [0, n), whatever the table holds.
+__device__ __forceinline__ void block_first_cursor(DescCursor& cur, const zero_tensor_desc* d,
+                                                   int64_t n, int64_t e) {
+    __shared__ int64_t s_k, s_off, s_numel, s_next;
+    __shared__ g_u16* s_ptr;
     if (threadIdx.x < 64) {
-        const int64_t k = wave_desc_at(d, n, e);
-        if (threadIdx.x == 0) s_first = k;
+        const int lane = threadIdx.x;
+        int64_t lo = 0, hi = n;           // lo == 0 or d[lo].offset <= e; answer in [lo - 1, hi)
+        int64_t k = -2;
+        while (hi - lo > 63) {
+            const int64_t step = (hi - lo + 63) / 64;
+            const int64_t j = lo + (int64_t)lane * step;
+            const int64_t oj = j < hi ? d[j].offset : INT64_MAX;
+            const int c = __popcll(__ballot(oj <= e));
+            if (c == 0) {                 // only when lo == 0: e lies before every tensor
+                k = -1;
+                if (lane == 0) s_next = oj;
+                break;
+            }
+            const int64_t nhi = lo + (int64_t)c * step;
+            lo = lo + (int64_t)(c - 1) * step;
+            hi = nhi < hi ? nhi : hi;
+        }
+        if (k == -2) {
+            // last round over [lo, hi] (at most 64 entries): every lane loads its
+            // whole candidate, so the one found and the next offset reach the
+            // block without another dependent load
+            const int64_t j = lo + lane;
+            const bool in_table = j < n;
+            const zero_tensor_desc dj = in_table ? d[j] : zero_tensor_desc{nullptr, INT64_MAX, 0, 0};
+            const int c = __popcll(__ballot(j < hi && dj.offset <= e));
+            k = lo + c - 1;
+            if (lane == c - 1) {
+                s_ptr = (g_u16*)dj.ptr;
+                s_off = dj.offset;
+                s_numel = dj.numel;
+            }
+            if (lane == c) s_next = in_table ? dj.offset : INT64_MAX;
+        }
+        if (lane == 0) s_k = k;
     }
     __syncthreads();
-    return s_first;
+    cur.k = s_k;
+    cur.ptr = s_k >= 0 ? s_ptr : nullptr;
+    cur.off = s_k >= 0 ? s_off : 0;
+    cur.numel = s_k >= 0 ? s_numel : 0;
+    cur.next = s_next;
 }
 
 // Copy between the flat buffer and the tensors the descriptors name
@@ -195,7 +210,7 @@ __device__ __forceinline__ void flat_copy(uint16_t* flat, const Split& s,
     DescCursor cur;
     cur.d = descs;
     cur.n = n_descs;
-    cur.load(block_first_desc(descs, n_descs, blk == 0 ? 0 : base));
+    block_first_cursor(cur, descs, n_descs, blk == 0 ? 0 : base);
     bool fast[kFlatRows], next_ok[kFlatRows], prev_ok[kFlatRows];
     int64_t e0[kFlatRows];
     uintptr_t q[kFlatRows];                 // tensor-side address of a fast tile
