@@ -292,6 +292,9 @@ def main():
         print(json.dumps({"error": "runs on one GPU only: the owner-shard step is "
                           "measured on one GPU's partition; run with --gpus 1"}), file=sys.stderr)
         sys.exit(2)
+    if args.write_back and args.workload != "buckets":
+        print(json.dumps({"error": "--write-back applies to --workload buckets"}), file=sys.stderr)
+        sys.exit(2)
     import numpy as np
     import torch
 
@@ -316,9 +319,6 @@ def main():
     copy_in = None
     write_back = None
     rr_info = None
-    if args.write_back and args.workload != "buckets":
-        print(json.dumps({"error": "--write-back applies to --workload buckets"}), file=sys.stderr)
-        sys.exit(2)
     if args.round_robin_owner is not None:
         shard, count_rr, n_owned, imbalance = build_round_robin(
             wl, args.round_robin_owner, arena=not args.no_arena,
