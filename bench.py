@@ -83,6 +83,10 @@ def parse():
                     help="separate allocations instead of one arena with spread placement")
     ap.add_argument("--min-gap-gib", type=float, default=0.0,
                     help="minimum distance between the AdamW streams' bases in the arena")
+    ap.add_argument("--flush-gib", type=float, default=0.0,
+                    help="write this much scratch memory between timed steps (untimed), so that "
+                         "no step finds its inputs in the 256 MB Infinity Cache or the L2; "
+                         "value and ms_per_step then come from the per-step events")
     ap.add_argument("--graph", action="store_true",
                     help="keep the loss scaler and step count on the device and replay one "
                          "captured HIP graph per step (no host round trip between steps)")
@@ -374,8 +378,13 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
+    flush = None
+    if args.flush_gib > 0:
+        flush = torch.empty(int(args.flush_gib * 2 ** 30) // 4, dtype=torch.float32, device="cuda")
     for k in range(args.steps):
         Z.zero_partition_layout(wl.numels, wl.world, wl.align)
+        if flush is not None:
+            flush.fill_(float(k))                  # evicts the caches; outside the step's events
         if graph is not None:
             ev[k][0].record()
             graph.replay()
@@ -424,12 +433,14 @@ def main():
         avg = float(np.mean(v))
         phases[k] = {"ms": round(avg, 4), "bytes_per_elem": bytes_per[k],
                      "GBps": round(bytes_per[k] * count / (avg * 1e-3) / 1e9, 1)}
-    step_ms = total_ms / args.steps
     # each step's own device time: from its first event (copy-in or reduce)
     # to its last (AdamW, or the write-back)
     first = 0 if (graph is not None or not copy_in) else 4
     last = 5 if (write_back and graph is None) else 3
     per_step = [e[first].elapsed_time(e[last]) for e in ev]
+    if flush is not None:                          # the flushes sit between the steps' events
+        total_ms = float(sum(per_step))
+    step_ms = total_ms / args.steps
     step_bytes = sum(bytes_per.values()) * count
     roofline = None
     if "adamw" in ms:
@@ -475,6 +486,7 @@ def main():
             "in_place_reduce": in_place,
             "fused_reduce_check": not args.unfused,
             "graph": bool(args.graph),
+            "flush_between_steps_gib": args.flush_gib,
             "placement": ("separate allocations" if args.no_arena else
                           f"one arena, AdamW streams interleaved with rank buffers, "
                           f"min gap {args.min_gap_gib:g} GiB"),
