@@ -182,7 +182,9 @@ reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, const zero_step_c
     double sq = 0.0;
     uint32_t bad = 0;
     const int64_t blk = block_id(s);
-    if (CHECK && ctl) inv = ctl->inv_scale;             // device-resident step control
+    // With device step control the unscale factor is read from ctl after the
+    // rank loads are issued: read before them, its scalar-load latency would
+    // sit in front of every block's HBM loads.
     if (s.aligned) {
         if (lane_tile<kReduceTiles>(s, kReduceTiles - 1) < s.nvec) {   // every row in range
             u32x4 w[kReduceTiles][NR];
@@ -192,6 +194,7 @@ reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, const zero_step_c
 #pragma unroll
                 for (int r = 0; r < NR; ++r) w[t][r] = load_nt(src.p[r] + e);
             }
+            if (CHECK && ctl) inv = ctl->inv_scale;
 #pragma unroll
             for (int t = 0; t < kReduceTiles; ++t)
                 reduce_tile<DT, NR, CHECK>(w[t], dst + s.head + lane_tile<kReduceTiles>(s, t) * kVec,
@@ -205,6 +208,7 @@ reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, const zero_step_c
                     u32x4 w[NR];
 #pragma unroll
                     for (int r = 0; r < NR; ++r) w[r] = load_nt(src.p[r] + e);
+                    if (CHECK && ctl) inv = ctl->inv_scale;
                     reduce_tile<DT, NR, CHECK>(w, dst + e, inv, sq, bad);
                 }
             }
@@ -216,12 +220,14 @@ reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, const zero_step_c
             else if (t >= 64 && t < 64 + kVec && s.head + s.nvec * kVec + (t - 64) < s.count)
                 e = s.head + s.nvec * kVec + (t - 64);
             if (e >= 0) {
+                if (CHECK && ctl) inv = ctl->inv_scale;
                 const uint16_t h = reduce_one<DT>(src, NR, e);
                 dst[e] = h;
                 if (CHECK) check_acc<DT>(h, inv, sq, bad);
             }
         }
     } else {
+        if (CHECK && ctl) inv = ctl->inv_scale;
         for (int t = 0; t < kReduceTiles; ++t) {
             const int64_t i = lane_tile<kReduceTiles>(s, t);
             for (int64_t e = i * kVec; e < (i + 1) * kVec && e < s.count; ++e) {
@@ -247,21 +253,23 @@ check_kernel(const uint16_t* __restrict__ g, Split s, float inv, const zero_step
              double* __restrict__ part_sum, uint32_t* __restrict__ part_flag) {
     double sq = 0.0;
     uint32_t bad = 0;
-    if (ctl) inv = ctl->inv_scale;                      // device-resident step control
     const int64_t i = lane_tile(s);
     if (s.aligned) {
         if (i < s.nvec) {
             const u32x4 w = load_nt(g + s.head + i * kVec);
+            if (ctl) inv = ctl->inv_scale;              // after the load is issued
 #pragma unroll
             for (int k = 0; k < kVec; ++k) check_acc<DT>(half_of(w, k), inv, sq, bad);
         }
         if (block_id(s) == 0) {
             const int t = threadIdx.x;
+            if (ctl) inv = ctl->inv_scale;
             if (t < s.head) check_acc<DT>(g[t], inv, sq, bad);
             else if (t >= 64 && t < 64 + kVec && s.head + s.nvec * kVec + (t - 64) < s.count)
                 check_acc<DT>(g[s.head + s.nvec * kVec + (t - 64)], inv, sq, bad);
         }
     } else {
+        if (ctl) inv = ctl->inv_scale;
         for (int64_t e = i * kVec; e < (i + 1) * kVec && e < s.count; ++e)
             check_acc<DT>(g[e], inv, sq, bad);
     }
