@@ -87,6 +87,11 @@ def parse():
                     help="write this much scratch memory between timed steps (untimed), so that "
                          "no step finds its inputs in the 256 MB Infinity Cache or the L2; "
                          "value and ms_per_step then come from the per-step events")
+    ap.add_argument("--inject-every", type=int, default=0,
+                    help="every K-th timed step, one rank's gradient holds +inf (odd "
+                         "occurrences) or NaN (even) at a seeded index: the step is skipped "
+                         "and the loss scale halves (the fragmented-bucket workload's overflow "
+                         "path); 0 = off")
     ap.add_argument("--graph", action="store_true",
                     help="keep the loss scaler and step count on the device and replay one "
                          "captured HIP graph per step (no host round trip between steps)")
@@ -296,6 +301,10 @@ def main():
         print(json.dumps({"error": "runs on one GPU only: the owner-shard step is "
                           "measured on one GPU's partition; run with --gpus 1"}), file=sys.stderr)
         sys.exit(2)
+    if args.inject_every < 0 or args.inject_every == 1:
+        print(json.dumps({"error": "--inject-every takes 0 (off) or K >= 2, so that some "
+                          "steps run whole"}), file=sys.stderr)
+        sys.exit(2)
     if args.write_back and args.workload != "buckets":
         print(json.dumps({"error": "--write-back applies to --workload buckets"}), file=sys.stderr)
         sys.exit(2)
@@ -381,21 +390,34 @@ def main():
     flush = None
     if args.flush_gib > 0:
         flush = torch.empty(int(args.flush_gib * 2 ** 30) // 4, dtype=torch.float32, device="cuda")
+    injections = 0
     for k in range(args.steps):
         Z.zero_partition_layout(wl.numels, wl.world, wl.align)
         if flush is not None:
             flush.fill_(float(k))                  # evicts the caches; outside the step's events
+        planted = None
+        if args.inject_every and (k + 1) % args.inject_every == 0:
+            # a rank whose buffer the copy-in does not rewrite; seeded index
+            injections += 1
+            r = 1 + (k % (len(bufs) - 1)) if len(bufs) > 1 else 0
+            idx = (k * 2654435761 + 12345) % count
+            bad = float("inf") if injections % 2 else float("nan")
+            planted = (bufs[r], idx, bufs[r][idx:idx + 1].clone())
+            bufs[r][idx:idx + 1].fill_(bad)
         if graph is not None:
             ev[k][0].record()
             graph.replay()
             ev[k][3].record()
-            continue
-        ev[k][4].record()
-        if copy_in:
-            copy_in()
-        info = one_step(marks=ev[k])
-        applied += info.applied
-        infos.append(info)
+        else:
+            ev[k][4].record()
+            if copy_in:
+                copy_in()
+            info = one_step(marks=ev[k])
+            applied += info.applied
+            infos.append(info)
+        if planted is not None:
+            buf, idx, old = planted
+            buf[idx:idx + 1].copy_(old)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -428,9 +450,13 @@ def main():
     if write_back and graph is None:
         ms["write_back"] = [e[3].elapsed_time(e[5]) for e in ev]
         bytes_per["write_back"] = 4
+    # steps that ran whole: an injected overflow makes AdamW return early, so
+    # phase rates, the roofline and step_GBps average over the other steps only
+    whole = [k for k in range(args.steps)
+             if not (args.inject_every and (k + 1) % args.inject_every == 0)]
     phases = {}
     for k, v in ms.items():
-        avg = float(np.mean(v))
+        avg = float(np.mean([v[i] for i in whole]))
         phases[k] = {"ms": round(avg, 4), "bytes_per_elem": bytes_per[k],
                      "GBps": round(bytes_per[k] * count / (avg * 1e-3) / 1e9, 1)}
     # each step's own device time: from its first event (copy-in or reduce)
@@ -441,10 +467,11 @@ def main():
     if flush is not None:                          # the flushes sit between the steps' events
         total_ms = float(sum(per_step))
     step_ms = total_ms / args.steps
+    whole_ms = step_ms if not args.inject_every else float(np.mean([per_step[i] for i in whole]))
     step_bytes = sum(bytes_per.values()) * count
     roofline = None
     if "adamw" in ms:
-        adam_avg_s = float(np.mean(ms["adamw"])) * 1e-3
+        adam_avg_s = float(np.mean([ms["adamw"][i] for i in whole])) * 1e-3
         achieved = 28 * count / adam_avg_s / 1e9
         roofline = {
             "bound": "hbm",
@@ -458,6 +485,9 @@ def main():
                             "factors from a known-size elementwise kernel)",
         }
 
+    if shard.ctl is not None:
+        shard.sync_control()
+    shard_scale = shard.scale
     result = {
         "metric": "params updated/s per GPU (ZeRO shard AdamW step) + achieved HBM GB/s % of peak",
         "value": count * applied / (total_ms * 1e-3),
@@ -487,15 +517,18 @@ def main():
             "fused_reduce_check": not args.unfused,
             "graph": bool(args.graph),
             "flush_between_steps_gib": args.flush_gib,
+            "inf_nan_every": args.inject_every,
             "placement": ("separate allocations" if args.no_arena else
                           f"one arena, AdamW streams interleaved with rank buffers, "
                           f"min gap {args.min_gap_gib:g} GiB"),
             "parallelism": "one owner partition on one GPU (N ranks simulated in HBM)",
         },
-        "step_GBps": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
-        "step_frac_of_peak": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_GBps": round(step_bytes / (whole_ms * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(step_bytes / (whole_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "phases": phases,
         "applied_steps": applied,
+        "skipped_steps": args.steps - applied,
+        "final_loss_scale": shard_scale,
         "per_step_ms": [round(x, 4) for x in per_step],
         "median_step_ms": round(float(np.median(per_step)), 4),
         "final_norm": (float(np.sqrt(infos[-1].sumsq)) if infos else

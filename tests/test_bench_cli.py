@@ -23,3 +23,10 @@ def test_write_back_needs_the_bucket_workload():
     r = _run("--write-back", "--workload", "llama7b")
     assert r.returncode == 2
     assert "buckets" in json.loads(r.stderr.strip().splitlines()[-1])["error"]
+
+
+def test_inject_every_needs_whole_steps():
+    for k in ("1", "-3"):
+        r = _run("--inject-every", k)
+        assert r.returncode == 2
+        assert "inject-every" in json.loads(r.stderr.strip().splitlines()[-1])["error"]
