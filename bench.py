@@ -64,7 +64,8 @@ def measured_traffic(kernel: str, workload: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 40 for the buckets workload)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama70b",
                     choices=["toy", "bert", "llama7b", "llama70b", "buckets"])
@@ -87,11 +88,11 @@ def parse():
                     help="write this much scratch memory between timed steps (untimed), so that "
                          "no step finds its inputs in the 256 MB Infinity Cache or the L2; "
                          "value and ms_per_step then come from the per-step events")
-    ap.add_argument("--inject-every", type=int, default=0,
+    ap.add_argument("--inject-every", type=int, default=None,
                     help="every K-th timed step, one rank's gradient holds +inf (odd "
                          "occurrences) or NaN (even) at a seeded index: the step is skipped "
-                         "and the loss scale halves (the fragmented-bucket workload's overflow "
-                         "path); 0 = off")
+                         "and the loss scale halves; 0 = off (default 4 for the buckets "
+                         "workload, whose protocol has an overflow every 4th step; else 0)")
     ap.add_argument("--graph", action="store_true",
                     help="keep the loss scaler and step count on the device and replay one "
                          "captured HIP graph per step (no host round trip between steps)")
@@ -301,6 +302,10 @@ def main():
         print(json.dumps({"error": "runs on one GPU only: the owner-shard step is "
                           "measured on one GPU's partition; run with --gpus 1"}), file=sys.stderr)
         sys.exit(2)
+    if args.steps is None:
+        args.steps = 40 if args.workload == "buckets" else 20
+    if args.inject_every is None:
+        args.inject_every = 4 if args.workload == "buckets" else 0
     if args.inject_every < 0 or args.inject_every == 1:
         print(json.dumps({"error": "--inject-every takes 0 (off) or K >= 2, so that some "
                           "steps run whole"}), file=sys.stderr)

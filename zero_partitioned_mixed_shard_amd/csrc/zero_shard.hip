@@ -433,7 +433,7 @@ adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restri
         store_f4(ma + e + 4, mo[1]);
         store_f4(va + e, vo[0]);
         store_f4(va + e + 4, vo[1]);
-        store_b128(p16 + e, pack8(ph));
+        store_nt(p16 + e, pack8(ph));                // written once: non-temporal
     }
     if (block_id(s) == 0) {
         const AdamConsts c = step_consts(c0, ctl);
