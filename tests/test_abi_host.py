@@ -147,3 +147,17 @@ def test_device_control_calls_reject_null_pointers_before_launching():
                                  None) == Z.ZERO_EINVAL
     assert L.zero_adamw_step_ctl(fake, fake, fake, fake, fake, 16, Z.ZERO_BF16, None, fake, fake,
                                  None) == Z.ZERO_EINVAL
+
+
+def test_builder_loads_without_the_package():
+    """build() must work on a tree where nothing is built yet: loading the
+    build module may not import the package, whose import needs the library."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(HEADER))
+    code = ("import sys, __graft_entry__ as g; m = g._load_builder(); "
+            "assert callable(m.build) and m.LIB.endswith('libzero_shard.so'); "
+            "assert 'zero_partitioned_mixed_shard_amd' not in sys.modules, sorted(sys.modules)")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
