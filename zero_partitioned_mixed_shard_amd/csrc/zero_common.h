@@ -29,6 +29,7 @@ constexpr int64_t kMaxLaunchBlocks = (int64_t(1) << 32) / kThreads - 1;
 constexpr unsigned kLdsPerCU = 160 * 1024;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // How the elements of a call map onto tiles.  With `aligned`, lanes run the
@@ -48,6 +49,12 @@ __device__ __forceinline__ u32x4 load_nt(const uint16_t* p) {
 __device__ __forceinline__ void store_nt(uint16_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
+__device__ __forceinline__ u32x2 load_nt_b64(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ void store_nt_b64(uint16_t* p, u32x2 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
 __device__ __forceinline__ u32x4 load_b128(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
@@ -62,6 +69,15 @@ __device__ __forceinline__ void store_f4(float* p, f32x4 v) {
 }
 __device__ __forceinline__ uint16_t half_of(u32x4 w, int k) {
     return (uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu));
+}
+__device__ __forceinline__ uint16_t half_of2(u32x2 w, int k) {
+    return (uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu));
+}
+__device__ __forceinline__ u32x2 pack4(const uint16_t* h) {
+    u32x2 w;
+    w[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    w[1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+    return w;
 }
 __device__ __forceinline__ u32x4 pack8(const uint16_t* h) {
     u32x4 w;
