@@ -340,6 +340,37 @@ def test_adamw_parity(dtype, count, offset, clip, t):
     assert_p16_close(to_np16(d_p16), p16, dtype, "param16")
 
 
+# Lane l of an AdamW block takes the element quads at 4l and 1024 + 4l of the
+# block's 2048 elements: these sizes end the vector body exactly at, just
+# before and just after the half-block boundary of the last block, and in the
+# middle of either half, so lanes with both quads, only the first, and none
+# all occur (with the misaligned offsets also through the head path).
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("count", [2048 + 1024, 2048 + 1020, 2048 + 1028, 3 * 2048 + 500 + 5,
+                                   5 * 2048 + 1600 + 7])
+@pytest.mark.parametrize("offset", [0, 1, 6])
+def test_adamw_half_block_edges(dtype, count, offset):
+    rng = np.random.default_rng(count + 31 * offset)
+    master, m, v = _state(count, rng)
+    p16 = oracle.encode16(master, dtype)
+    grad = _rand16(count, dtype, rng, sigma=1e-3, scale=1.0)
+    hp = oracle.HParams(max_grad_norm=1.0)
+    d_master, d_m, d_v = _dev32(master, offset), _dev32(m, offset), _dev32(v, offset)
+    d_p16, d_g = _dev16(p16, dtype, offset), _dev16(grad, dtype, offset)
+    res = _res_tensor()
+    Z.zero_unscale_check_norm(d_g, 1.0, res, _ws(count))
+    Z.zero_adamw_step(d_master, d_m, d_v, d_p16, d_g,
+                      Z.zero_adamw_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
+                                           hp.max_grad_norm, 2), res)
+    torch.cuda.synchronize()
+    flag, sumsq = oracle.check(grad, dtype, 1.0)
+    oracle.adamw(master, m, v, p16, grad, dtype, 1.0, sumsq, flag, hp, 2)
+    assert_f32_close(to_np32(d_master), master, "master")
+    assert_f32_close(to_np32(d_m), m, "exp_avg")
+    assert_f32_close(to_np32(d_v), v, "exp_avg_sq")
+    assert_p16_close(to_np16(d_p16), p16, dtype, "param16")
+
+
 @pytest.mark.parametrize("dtype", [FP16, BF16])
 def test_adamw_bit_exact_large(dtype):
     """On a large aligned shard the fp32 results are expected to be bit-equal."""
