@@ -82,6 +82,11 @@ def parse():
                          "i mod N == this owner (packed; one reduce window per tensor)")
     ap.add_argument("--no-arena", action="store_true",
                     help="separate allocations instead of one arena with spread placement")
+    ap.add_argument("--placement", default="auto",
+                    choices=["auto", "interleaved", "rank_block", "rank_block_b", "master_ranks",
+                             "streams_first", "ranks_first"],
+                    help="order of the buffers in the arena; auto times every order once at "
+                         "setup (outside the timed steps) and keeps the fastest")
     ap.add_argument("--min-gap-gib", type=float, default=0.0,
                     help="minimum distance between the AdamW streams' bases in the arena")
     ap.add_argument("--flush-gib", type=float, default=0.0,
@@ -168,7 +173,7 @@ def cpu_baseline(wl, begin: int, seconds: float) -> dict:
 
 
 def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
-                device_control: bool = False):
+                device_control: bool = False, placement: str = "auto"):
     """Owner 0's shard of `wl` as the bench runs it: state, reduced gradient
     and the N rank buffers (the LLaMA-70B shard reduces in place into rank 0's
     buffer), initial 16-bit weights and one gradient batch generated on the
@@ -187,7 +192,7 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
                       window=wl.window, in_place_rank=0 if in_place else None, fused=fused,
                       own_ranks=True, world=wl.world, arena=arena, min_gap=min_gap,
-                      device_control=device_control)
+                      device_control=device_control, placement=placement)
     shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16))
     for r, buf in enumerate(shard.rank_bufs):
         I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded, out=buf)
@@ -196,7 +201,8 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
 
 
 def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
-                  write_back: bool = False, device_control: bool = False):
+                  write_back: bool = False, device_control: bool = False,
+                  placement: str = "auto"):
     """The 10,000-tensor group with all N owners on this GPU, as the bench runs
     it: rank 0's gradient arrives as one separate device tensor per parameter
     (10,000 allocations) and is copied into rank 0's flat buffer bucket by
@@ -222,7 +228,8 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                       eps=wl.eps, weight_decay=wl.weight_decay, max_grad_norm=wl.clip,
                       scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window,
                       windows=windows, fused=fused, own_ranks=True, world=wl.world,
-                      arena=arena, min_gap=min_gap, device_control=device_control)
+                      arena=arena, min_gap=min_gap, device_control=device_control,
+                      placement=placement)
     shard.load_param16(I.device_param16(wl, offs, 0, padded, out=shard.param16))
     for r, buf in enumerate(shard.rank_bufs):
         I.device_rank_grad(wl, 1, wl.scale0, r, 0, padded, padded, out=buf)
@@ -256,7 +263,7 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
 
 
 def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fused: bool = True,
-                      device_control: bool = False):
+                      device_control: bool = False, placement: str = "auto"):
     """Round-robin inter-tensor ownership (ZeRO 优化器, "参数分配策略"): this
     owner holds the whole tensors i with i mod N == owner, packed back to back
     (state only for what it owns); each tensor is reduced to it on its own
@@ -284,7 +291,7 @@ def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fuse
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
                       window=wl.window, windows=windows, fused=fused, own_ranks=True,
                       world=wl.world, arena=arena, min_gap=min_gap,
-                      device_control=device_control)
+                      device_control=device_control, placement=placement)
     for k, i in enumerate(owned):
         a, b = packed[k], packed[k + 1]
         g0 = int(offs[i])
@@ -341,19 +348,20 @@ def main():
         shard, count_rr, n_owned, imbalance = build_round_robin(
             wl, args.round_robin_owner, arena=not args.no_arena,
             min_gap=int(args.min_gap_gib * 2 ** 30), fused=not args.unfused,
-            device_control=args.graph)
+            device_control=args.graph, placement=args.placement)
         begin, end, padded, in_place = 0, count_rr, 0, False
         rr_info = {"owner": args.round_robin_owner, "owned_tensors": n_owned,
                    "owned_elems": count_rr, "largest_over_mean_owner": round(imbalance, 4)}
     elif args.workload == "buckets":
         shard, copy_in, padded, write_back = build_buckets(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
-            fused=not args.unfused, write_back=args.write_back, device_control=args.graph)
+            fused=not args.unfused, write_back=args.write_back, device_control=args.graph,
+            placement=args.placement)
         begin, end, in_place = 0, padded, False
     else:
         shard, begin, end, padded, in_place = build_shard(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
-            fused=not args.unfused, device_control=args.graph)
+            fused=not args.unfused, device_control=args.graph, placement=args.placement)
     count = end - begin
     bufs = shard.rank_bufs
 
@@ -524,8 +532,11 @@ def main():
             "flush_between_steps_gib": args.flush_gib,
             "inf_nan_every": args.inject_every,
             "placement": ("separate allocations" if args.no_arena else
-                          f"one arena, AdamW streams interleaved with rank buffers, "
-                          f"min gap {args.min_gap_gib:g} GiB"),
+                          f"one arena, buffer order {shard.placement}"
+                          + (" (fastest of the orders timed at setup)"
+                             if args.placement == "auto" else "")
+                          + f", min gap {args.min_gap_gib:g} GiB"),
+            "placement_setup_ms": shard.placement_ms or None,
             "parallelism": "one owner partition on one GPU (N ranks simulated in HBM)",
         },
         "step_GBps": round(step_bytes / (whole_ms * 1e-3) / 1e9, 1),

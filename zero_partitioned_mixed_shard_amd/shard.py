@@ -23,12 +23,25 @@ the result and the control back for reporting.
 
 Placement.  With own_ranks=True the step also holds the N simulated rank
 buffers.  With arena=True every large buffer is carved from one device
-allocation in an order that keeps the arrays AdamW streams together (master,
-m, v, the 16-bit copy, the reduced gradient) far apart in HBM, rank buffers
-in between; `min_gap` bytes additionally puts each of those five arrays at
-least that far from the previous one.  On MI355X, streams whose base
-addresses are 32 GiB or more apart sustain about 15 % more bandwidth in the
-AdamW pass than streams packed back to back.
+allocation, in one of the orders of ARENA_ORDERS (`placement`):
+  interleaved   the arrays AdamW streams (master, m, v, the 16-bit copy, the
+                reduced gradient) with rank buffers between them;
+  rank_block    16-bit copy, master, m, then all rank buffers in rank order
+                (the reduced gradient right after them), then v;
+  rank_block_b  master, m, 16-bit copy, rank buffers, reduced gradient, v;
+  master_ranks  master, rank buffers, reduced gradient, m, v, 16-bit copy;
+  streams_first the AdamW arrays, then the rank buffers;
+  ranks_first   the rank buffers, then the AdamW arrays.
+`min_gap` bytes additionally puts each AdamW array at least that far from the
+previous one.  On MI355X the HBM bandwidth of both passes depends on where
+the arrays sit in physical memory, which a process cannot see: the same
+buffers at the same offsets run at different rates in arenas of different
+sizes, and the same rank buffers of the LLaMA-70B shard reduce at 6.1 to
+6.5 TB/s depending on where their block starts.  With placement="auto" the
+step therefore measures: it zeroes the arena, times two steps of the real
+call sequence in every order, three more for the two fastest, and keeps the
+fastest (`placement_ms` holds the times).  That costs three steps per order
+and six more at construction, and no memory beyond the arena.
 
 Nothing here computes on the data; it sequences calls and keeps host scalars.
 """
@@ -48,6 +61,55 @@ from . import (RESULT_BYTES, ZERO_BF16, ZERO_FP16, control_to_device, read_contr
                zero_unscale_check_norm, zero_unscale_check_norm_ctl)
 
 
+def _interleaved(names, streams, in_place):
+    """AdamW arrays with rank buffers between them (remaining ranks last)."""
+    st = [nm for nm in names if nm in streams]
+    rk = [nm for nm in names if nm not in streams]
+    seq = []
+    for k, nm in enumerate(st):
+        seq.append(nm)
+        if k < len(rk):
+            seq.append(rk[k])
+    return seq + rk[len(st):]
+
+
+def _rank_block(head):
+    """`head` arrays, all rank buffers in rank order, the separate reduced
+    gradient, then the AdamW arrays not yet placed."""
+    def order(names, streams, in_place):
+        rk = _rank_names(names)
+        first = [nm for nm in head if nm in names]
+        red = ["red"] if "red" in names else []
+        rest = [nm for nm in names if nm not in first and nm not in rk and nm not in red]
+        return first + rk + red + rest
+    return order
+
+
+def _rank_names(names):
+    return sorted((nm for nm in names if nm.startswith("rank")), key=lambda x: int(x[4:]))
+
+
+def _streams_first(names, streams, in_place):
+    """The AdamW arrays (and a separate reduced gradient), then the ranks."""
+    return [nm for nm in names if not nm.startswith("rank")] + _rank_names(names)
+
+
+def _ranks_first(names, streams, in_place):
+    """The rank buffers, then the AdamW arrays."""
+    return _rank_names(names) + [nm for nm in names if not nm.startswith("rank")]
+
+
+# Buffer orders an arena can be laid out in (see the module docstring).
+ARENA_ORDERS = {
+    "interleaved": _interleaved,
+    "rank_block": _rank_block(["param16", "master", "exp_avg"]),
+    "rank_block_b": _rank_block(["master", "exp_avg", "param16"]),
+    "master_ranks": _rank_block(["master"]),
+    "streams_first": _streams_first,
+    "ranks_first": _ranks_first,
+}
+
+
 @dataclass
 class StepInfo:
     overflow: int
@@ -65,7 +127,8 @@ class ShardStep:
                  scale0=1.0, min_scale=1.0, window=1000, windows: Optional[Sequence[Tuple[int, int]]] = None,
                  divisor: int = 1, in_place_rank: Optional[int] = None, fused: bool = True,
                  own_ranks: bool = False, world: int = 0, arena: bool = False,
-                 min_gap: int = 0, device_control: bool = False, device="cuda"):
+                 min_gap: int = 0, device_control: bool = False, placement: str = "interleaved",
+                 device="cuda"):
         self.begin, self.end = begin, end
         self.count = end - begin
         self.owners = [(a - begin, b - begin) for a, b in owners]
@@ -91,57 +154,110 @@ class ShardStep:
         n_ranks = world if own_ranks else 0
         if own_ranks and world < 1:
             raise ValueError("own_ranks needs world >= 1")
-        bufs = self._allocate(n, n_ranks, in_place_rank is None, arena, min_gap, device)
-        self.master, self.exp_avg, self.exp_avg_sq = bufs["master"], bufs["exp_avg"], bufs["exp_avg_sq"]
-        self.param16 = bufs["param16"]
-        self.red = bufs.get("red")
-        self.rank_bufs = [bufs[f"rank{r}"] for r in range(n_ranks)]
-        self.exp_avg.zero_()
-        self.exp_avg_sq.zero_()
+        if placement != "auto" and placement not in ARENA_ORDERS:
+            raise ValueError(f"placement: one of {sorted(ARENA_ORDERS)} or 'auto'")
+        self.n_ranks = n_ranks
         self.res = torch.zeros(RESULT_BYTES // 4, dtype=torch.int32, device=device)
         self.ctl = None
-        if device_control:
-            self.ctl = control_to_device(zero_step_control_init(
-                scale0, min_scale, window, float(divisor), beta1, beta2), device=device)
         spans = [b - a for a, b in self.owners] + [b - a for a, b in self.reduce_ranges]
         ws = max(zero_check_workspace_bytes(n) for n in spans) if spans else 64
         self.workspace = torch.empty((ws + 7) // 8, dtype=torch.float64, device=device)
+        self.placement = placement if arena else "separate"
+        self.placement_ms = {}
+        self._allocate(n, n_ranks, in_place_rank is None, arena, min_gap, placement, device)
+        self.exp_avg.zero_()
+        self.exp_avg_sq.zero_()
+        if device_control:
+            self.ctl = control_to_device(zero_step_control_init(
+                scale0, min_scale, window, float(divisor), beta1, beta2), device=device)
 
     # ----------------------------------------------------------- placement
-    def _allocate(self, n, n_ranks, separate_red, arena, min_gap, device):
+    def _allocate(self, n, n_ranks, separate_red, arena, min_gap, placement, device):
         f32, b16 = (torch.float32, 4), (self.tdtype, 2)
         streams = [("master", f32), ("exp_avg", f32), ("exp_avg_sq", f32), ("param16", b16)]
         ranks = [(f"rank{r}", b16) for r in range(n_ranks)]
         if separate_red:
             streams.append(("red", b16))
-        elif self.in_place_rank is not None and self.in_place_rank < n_ranks:
-            # the reduced gradient lives in the owner's own rank buffer: an AdamW stream
-            k = self.in_place_rank
-            streams.append(ranks.pop(k))
         if not arena:
-            return {name: torch.empty(n, dtype=dt, device=device)
-                    for name, (dt, _) in streams + ranks}
-        # AdamW streams interleaved with rank buffers, each stream at least
-        # `min_gap` bytes after the previous stream's start
+            self._set_views({name: torch.empty(n, dtype=dt, device=device)
+                             for name, (dt, _) in streams + ranks})
+            return
+        names = [nm for nm, _ in streams + ranks]
+        kinds = dict(streams + ranks)
+        stream_set = {nm for nm, _ in streams}
+        if self.in_place_rank is not None and self.in_place_rank < n_ranks:
+            # the reduced gradient lives in the owner's own rank buffer: an AdamW stream
+            stream_set.add(f"rank{self.in_place_rank}")
+        orders = ARENA_ORDERS if placement == "auto" else {placement: ARENA_ORDERS[placement]}
+        plans = {}
+        for name, order_fn in orders.items():
+            seq = order_fn(names, stream_set, self.in_place_rank)
+            assert sorted(seq) == sorted(names), (name, seq)
+            plans[name] = self._place(seq, kinds, stream_set, n, min_gap)
+        size = max(end for _, end in plans.values())
+        self.arena = torch.empty(max(size, 1), dtype=torch.uint8, device=device)
+        if len(plans) == 1 or n_ranks == 0:
+            best = next(iter(plans))
+        else:
+            best = self._tune(plans, kinds, n)
+        self.placement = best
+        self._set_views(self._carve(plans[best][0], kinds, n))
+
+    @staticmethod
+    def _place(seq, kinds, stream_set, n, min_gap):
+        """Byte offsets of the buffers laid out in `seq` order (64 KiB
+        aligned), each AdamW array at least `min_gap` after the previous one."""
         align = 1 << 16
-        order = []
-        for k, st in enumerate(streams):
-            order.append((st, True))
-            if k < len(ranks):
-                order.append((ranks[k], False))
-        order += [(r, False) for r in ranks[len(streams):]]
         offs, cur, last_stream = {}, 0, None
-        for (name, (dt, size)), is_stream in order:
+        for name in seq:
+            is_stream = name in stream_set
             if is_stream and last_stream is not None:
                 cur = max(cur, last_stream + min_gap)
             cur = (cur + align - 1) // align * align
-            offs[name] = (cur, dt)
+            offs[name] = cur
             if is_stream:
                 last_stream = cur
-            cur += n * size
-        self.arena = torch.empty(max(cur, 1), dtype=torch.uint8, device=device)
-        return {name: self.arena[o:o + n * torch.tensor([], dtype=dt).element_size()].view(dt)
-                for name, (o, dt) in offs.items()}
+            cur += n * kinds[name][1]
+        return offs, cur
+
+    def _carve(self, offs, kinds, n):
+        return {name: self.arena[o:o + n * kinds[name][1]].view(kinds[name][0])
+                for name, o in offs.items()}
+
+    def _set_views(self, bufs):
+        self.master, self.exp_avg, self.exp_avg_sq = bufs["master"], bufs["exp_avg"], bufs["exp_avg_sq"]
+        self.param16 = bufs["param16"]
+        self.red = bufs.get("red")
+        self.rank_bufs = [bufs[f"rank{r}"] for r in range(self.n_ranks)]
+
+    def _tune(self, plans, kinds, n) -> str:
+        """Times the step's own calls (reduce windows, check, AdamW per owner)
+        in every order on a zeroed arena and returns the fastest.  Zero
+        gradients raise no overflow, so every pass runs whole (HBM rates on
+        MI355X were measured to be the same for random and constant data)."""
+        self.arena.zero_()
+        for name, (offs, _) in plans.items():
+            self._set_views(self._carve(offs, kinds, n))
+            self.launch()
+            self.placement_ms[name] = self._time_steps(2)
+        # the two fastest again, three more steps each: close calls are
+        # decided by more than two samples
+        for name in sorted(self.placement_ms, key=self.placement_ms.get)[:2]:
+            self._set_views(self._carve(plans[name][0], kinds, n))
+            self.placement_ms[name] = min(self.placement_ms[name], self._time_steps(3))
+        return min(self.placement_ms, key=self.placement_ms.get)
+
+    def _time_steps(self, k: int) -> float:
+        """Shortest of k timed launches of the step's calls (ms)."""
+        times = []
+        for _ in range(k):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            self.launch()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        return round(min(times), 4)
 
     # ---------------------------------------------------------------- state
     def load_param16(self, param16: torch.Tensor) -> None:
