@@ -161,3 +161,28 @@ def test_builder_loads_without_the_package():
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 0, r.stderr
+
+
+@pytest.mark.parametrize("n_ranks,in_place", [(0, None), (1, 0), (8, None), (8, 0), (8, 5),
+                                              (16, None), (16, 15)])
+def test_arena_orders_place_every_buffer_once(n_ranks, in_place):
+    """Every arena order is a permutation of the step's buffers, and the
+    placement gives each one a 64 KiB aligned, non-overlapping range, with
+    the AdamW arrays at least min_gap apart."""
+    from zero_partitioned_mixed_shard_amd.shard import ARENA_ORDERS, ShardStep
+    names = ["master", "exp_avg", "exp_avg_sq", "param16"] + (["red"] if in_place is None else [])
+    names += [f"rank{r}" for r in range(n_ranks)]
+    streams = set(names[:4]) | ({"red"} if in_place is None else {f"rank{in_place}"})
+    kinds = {nm: (None, 4 if nm in ("master", "exp_avg", "exp_avg_sq") else 2) for nm in names}
+    n = 1_000_003
+    for name, order in ARENA_ORDERS.items():
+        seq = order(names, streams, in_place)
+        assert sorted(seq) == sorted(names), name
+        for gap in (0, 3 << 20):
+            offs, end = ShardStep._place(seq, kinds, streams, n, gap)
+            spans = sorted((offs[nm], offs[nm] + n * kinds[nm][1]) for nm in names)
+            assert all(a % (1 << 16) == 0 for a, _ in spans)
+            assert all(b <= c for (_, b), (c, _) in zip(spans, spans[1:])), name
+            assert spans[-1][1] == end
+            st = sorted(offs[nm] for nm in streams)
+            assert all(b - a >= gap for a, b in zip(st, st[1:])), name

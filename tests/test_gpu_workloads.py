@@ -18,7 +18,7 @@ import synth
 from synth import inputs as I
 from synth import workloads as W
 import zero_partitioned_mixed_shard_amd as Z
-from zero_partitioned_mixed_shard_amd.shard import ShardStep
+from zero_partitioned_mixed_shard_amd.shard import ARENA_ORDERS, ShardStep
 from _common import (REL_TOL_NORM, assert_bits16_equal, assert_f32_close, assert_p16_close,
                      to_np16, to_np32)
 
@@ -50,14 +50,19 @@ def _setup(wl, owner_ids, round_robin=False):
 
 
 def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=False,
-               device_control=False):
+               device_control=False, placement=None, in_place_rank=None):
+    """placement: None for separate rank buffers handed to each step, else
+    the arena order of a step that holds its own rank buffers."""
     wl = W.WORKLOADS[name]
     steps = wl.steps if steps is None else steps
     offs, padded, owners, begin, end, windows = _setup(wl, owner_ids, round_robin)
+    arena = placement is not None
     shard = ShardStep(begin, end, owners, wl.dtype, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
                       eps=wl.eps, weight_decay=wl.weight_decay, max_grad_norm=wl.clip,
                       scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window, windows=windows,
-                      fused=fused, device_control=device_control)
+                      fused=fused, device_control=device_control, own_ranks=arena,
+                      world=wl.world if arena else 0, arena=arena,
+                      placement=placement or "interleaved", in_place_rank=in_place_rank)
     # initial state: device generator on the GPU, host generator for the oracle
     d_p16 = I.device_param16(wl, offs, begin, end)
     h_p16 = I.host_param16(wl, offs, begin, end, threads)
@@ -67,8 +72,8 @@ def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=F
               for a, b in owners]
     scaler = oracle.Scaler(wl.scale0, wl.min_scale, wl.window)
     t = 0
-    rank_bufs = [torch.empty(end - begin, dtype=shard.tdtype, device="cuda")
-                 for _ in range(wl.world)]
+    rank_bufs = shard.rank_bufs if arena else \
+        [torch.empty(end - begin, dtype=shard.tdtype, device="cuda") for _ in range(wl.world)]
     skipped = 0
     for s in range(1, steps + 1):
         assert shard.scale == scaler.scale
@@ -128,6 +133,33 @@ def test_round_robin_all_owners_equals_flat_union():
     """Every owner under round-robin ownership together updates every tensor
     exactly once: the same result as all owners of the flat layout."""
     run_parity("toy_tiny", list(range(8)), steps=3, round_robin=True)
+
+
+@pytest.mark.parametrize("placement", sorted(ARENA_ORDERS) + ["auto"])
+@pytest.mark.parametrize("in_place_rank", [None, 0, 5])
+def test_arena_orders_parity(placement, in_place_rank):
+    """The step holds its rank buffers in one arena, in every buffer order
+    and with the order measured at construction: the results do not depend
+    on where the buffers sit (in place: the reduced gradient overwrites that
+    rank's buffer).  The small ToyModel for the fixed orders, the full one's
+    partition 2 for the measured order."""
+    name = "toy" if placement == "auto" else "toy_tiny"
+    shard, _, _, _ = run_parity(name, [2], steps=3, placement=placement,
+                                in_place_rank=in_place_rank)
+    assert shard.placement in ARENA_ORDERS
+    if placement == "auto":
+        assert set(shard.placement_ms) == set(ARENA_ORDERS)
+        assert shard.placement == min(shard.placement_ms, key=shard.placement_ms.get)
+    else:
+        assert shard.placement == placement and not shard.placement_ms
+
+
+def test_arena_auto_buckets_all_owners():
+    """Measured placement with 16 owners, bucket windows and an overflow
+    every 4th step."""
+    shard, scaler, skipped, t = run_parity("buckets_small", list(range(16)), steps=8,
+                                           placement="auto")
+    assert skipped == 2 and t == 6
 
 
 @pytest.mark.parametrize("fused", [True, False])
