@@ -4,7 +4,9 @@ One step = the whole owner-shard path over one batch of synthetic gradients
 already resident in HBM:
   layout (host) -> reduce N ranks' 16-bit gradients to the owner fused with
   unscale + overflow check + squared norm (HIP) -> fused AdamW + 16-bit copy
-  (HIP) -> 16-byte result readback -> loss-scale update (host)
+  (HIP) -> loss-scale update and step count (HIP, device-resident step
+  control: no host round trip between steps; --host-control reads the
+  16-byte result back and updates the scaler on the host instead)
 Algorithmic HBM bytes per owned element: 2N + 2 for reduce+check (2N + 4 with
 --unfused, which re-reads the reduced gradient), 28 for AdamW.
 
@@ -98,6 +100,11 @@ def parse():
                          "occurrences) or NaN (even) at a seeded index: the step is skipped "
                          "and the loss scale halves; 0 = off (default 4 for the buckets "
                          "workload, whose protocol has an overflow every 4th step; else 0)")
+    ap.add_argument("--host-control", action="store_true",
+                    help="keep the loss scaler and step count on the host: every step ends with "
+                         "a 16-byte result readback (the GPU idles while the host updates the "
+                         "scaler and enqueues the next step); default: device-resident step "
+                         "control, no per-step round trip")
     ap.add_argument("--graph", action="store_true",
                     help="keep the loss scaler and step count on the device and replay one "
                          "captured HIP graph per step (no host round trip between steps)")
@@ -317,6 +324,10 @@ def main():
         print(json.dumps({"error": "--inject-every takes 0 (off) or K >= 2, so that some "
                           "steps run whole"}), file=sys.stderr)
         sys.exit(2)
+    if args.graph and args.host_control:
+        print(json.dumps({"error": "--graph replays a step with device-resident control; it "
+                          "cannot be combined with --host-control"}), file=sys.stderr)
+        sys.exit(2)
     if args.write_back and args.workload != "buckets":
         print(json.dumps({"error": "--write-back applies to --workload buckets"}), file=sys.stderr)
         sys.exit(2)
@@ -348,32 +359,36 @@ def main():
         shard, count_rr, n_owned, imbalance = build_round_robin(
             wl, args.round_robin_owner, arena=not args.no_arena,
             min_gap=int(args.min_gap_gib * 2 ** 30), fused=not args.unfused,
-            device_control=args.graph, placement=args.placement)
+            device_control=not args.host_control, placement=args.placement)
         begin, end, padded, in_place = 0, count_rr, 0, False
         rr_info = {"owner": args.round_robin_owner, "owned_tensors": n_owned,
                    "owned_elems": count_rr, "largest_over_mean_owner": round(imbalance, 4)}
     elif args.workload == "buckets":
         shard, copy_in, padded, write_back = build_buckets(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
-            fused=not args.unfused, write_back=args.write_back, device_control=args.graph,
-            placement=args.placement)
+            fused=not args.unfused, write_back=args.write_back,
+            device_control=not args.host_control, placement=args.placement)
         begin, end, in_place = 0, padded, False
     else:
         shard, begin, end, padded, in_place = build_shard(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
-            fused=not args.unfused, device_control=args.graph, placement=args.placement)
+            fused=not args.unfused, device_control=not args.host_control, placement=args.placement)
     count = end - begin
     bufs = shard.rank_bufs
 
 
     def one_step(marks=None):
+        """Enqueue one step.  With device-resident control nothing is read
+        back (the loss scale and step count advance on the device); with
+        host control the 16-byte result is read and the scaler updated."""
+        shard.launch(bufs, marks)
         if write_back:
-            shard.launch(bufs, marks)
             write_back()
             if marks:
                 marks[5].record()
-            return shard.finish()
-        return shard.step(bufs, marks=marks)
+        if shard.ctl is not None:
+            return None
+        return shard.finish()
 
     for _ in range(args.warmup):
         Z.zero_partition_layout(wl.numels, wl.world, wl.align)
@@ -387,12 +402,14 @@ def main():
     infos = []
     last_sumsq = None
     graph = None
+    t_before = None
+    if shard.ctl is not None:
+        shard.sync_control()
+        t_before = shard.t
     if args.graph:
         # one captured step (copy-in, reduce+check windows, AdamW per owner,
         # control update, write-back), replayed: per-step events bracket each
         # replay, phases inside the graph are not separated
-        shard.sync_control()
-        t_before = shard.t
         graph = shard.capture(bufs, before=copy_in, after=write_back)
         torch.cuda.synchronize()
     torch.cuda.synchronize()
@@ -426,8 +443,9 @@ def main():
             if copy_in:
                 copy_in()
             info = one_step(marks=ev[k])
-            applied += info.applied
-            infos.append(info)
+            if info is not None:
+                applied += info.applied
+                infos.append(info)
         if planted is not None:
             buf, idx, old = planted
             buf[idx:idx + 1].copy_(old)
@@ -435,7 +453,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
-    if graph is not None:
+    if shard.ctl is not None:
         shard.sync_control()
         applied = shard.t - t_before
         last_sumsq = Z.read_result(shard.res).sumsq
@@ -501,6 +519,8 @@ def main():
     if shard.ctl is not None:
         shard.sync_control()
     shard_scale = shard.scale
+    last = infos[-1].sumsq if infos else last_sumsq
+    final_norm = float(np.sqrt(last)) if last is not None and np.isfinite(last) else None
     result = {
         "metric": "params updated/s per GPU (ZeRO shard AdamW step) + achieved HBM GB/s % of peak",
         "value": count * applied / (total_ms * 1e-3),
@@ -528,6 +548,8 @@ def main():
             "clip": wl.clip,
             "in_place_reduce": in_place,
             "fused_reduce_check": not args.unfused,
+            "step_control": "host (16-byte readback per step)" if args.host_control else
+                            "device-resident (no per-step readback)",
             "graph": bool(args.graph),
             "flush_between_steps_gib": args.flush_gib,
             "inf_nan_every": args.inject_every,
@@ -547,8 +569,8 @@ def main():
         "final_loss_scale": shard_scale,
         "per_step_ms": [round(x, 4) for x in per_step],
         "median_step_ms": round(float(np.median(per_step)), 4),
-        "final_norm": (float(np.sqrt(infos[-1].sumsq)) if infos else
-                       float(np.sqrt(last_sumsq)) if last_sumsq is not None else None),
+        # the last step's norm; null when that step overflowed (no finite norm)
+        "final_norm": final_norm,
         "host_wall_s": round(wall, 4),
         "roofline": roofline,
     }

@@ -30,3 +30,9 @@ def test_inject_every_needs_whole_steps():
         r = _run("--inject-every", k)
         assert r.returncode == 2
         assert "inject-every" in json.loads(r.stderr.strip().splitlines()[-1])["error"]
+
+
+def test_graph_needs_device_control():
+    r = _run("--graph", "--host-control")
+    assert r.returncode == 2
+    assert "host-control" in json.loads(r.stderr.strip().splitlines()[-1])["error"]
