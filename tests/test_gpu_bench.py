@@ -1,0 +1,49 @@
+"""bench.py end to end on the GPU, on the small shards: one JSON line with
+the fields of its contract, whole steps counted, the roofline entry present,
+and the measured placement reported (device-resident and host step control,
+and the inf/NaN protocol of the fragmented-bucket workload)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FIELDS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+          "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config", "roofline")
+
+
+def _bench(*args):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--no-cpu-baseline", *args],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = r.stdout.strip().splitlines()[-1]
+    return json.loads(line)
+
+
+@pytest.mark.parametrize("control", [[], ["--host-control"]])
+def test_toy_json_line(control):
+    b = _bench("--workload", "toy", "--steps", "4", "--warmup", "1", *control)
+    for f in FIELDS:
+        assert f in b, f
+    assert b["n_gpus"] == 1 and b["steps"] == 4 and b["applied_steps"] == 4
+    assert b["value"] > 0 and b["ms_per_step"] > 0
+    assert "model" not in b["config"] and "workload" in b["config"]
+    r = b["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and 0 < r["frac"] < 1
+    assert r["achieved"] == pytest.approx(28 * b["config"]["owned_elems"]
+                                          / (b["phases"]["adamw"]["ms"] * 1e-3) / 1e9, rel=1e-3)
+    assert b["config"]["placement_setup_ms"] and "buffer order" in b["config"]["placement"]
+    assert b["final_norm"] is not None and b["final_norm"] > 0
+
+
+def test_buckets_overflow_protocol():
+    """An inf/NaN every 4th step: those steps are skipped and halve the
+    scale (16 steps: 4 skipped, 2^16 / 2^4)."""
+    b = _bench("--workload", "buckets", "--steps", "16", "--warmup", "1")
+    assert b["applied_steps"] == 12 and b["skipped_steps"] == 4
+    assert b["final_loss_scale"] == 2.0 ** 12
+    assert b["final_norm"] is None              # the last step overflowed
