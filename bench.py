@@ -89,6 +89,11 @@ def parse():
                              "streams_first", "ranks_first"],
                     help="order of the buffers in the arena; auto times every order once at "
                          "setup (outside the timed steps) and keeps the fastest")
+    ap.add_argument("--arena-slack-gib", type=float, default=20.0,
+                    help="allocate the arena up to this much larger (never more than is free, "
+                         "less 4 GiB) and let --placement auto also try every order shifted by "
+                         "it, i.e. at other physical addresses; 0 = an arena of exactly the "
+                         "working set")
     ap.add_argument("--min-gap-gib", type=float, default=0.0,
                     help="minimum distance between the AdamW streams' bases in the arena")
     ap.add_argument("--flush-gib", type=float, default=0.0,
@@ -180,7 +185,7 @@ def cpu_baseline(wl, begin: int, seconds: float) -> dict:
 
 
 def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
-                device_control: bool = False, placement: str = "auto"):
+                device_control: bool = False, placement: str = "auto", arena_slack: int = 0):
     """Owner 0's shard of `wl` as the bench runs it: state, reduced gradient
     and the N rank buffers (the LLaMA-70B shard reduces in place into rank 0's
     buffer), initial 16-bit weights and one gradient batch generated on the
@@ -199,7 +204,8 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
                       window=wl.window, in_place_rank=0 if in_place else None, fused=fused,
                       own_ranks=True, world=wl.world, arena=arena, min_gap=min_gap,
-                      device_control=device_control, placement=placement)
+                      device_control=device_control, placement=placement,
+                      arena_slack=arena_slack)
     shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16))
     for r, buf in enumerate(shard.rank_bufs):
         I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded, out=buf)
@@ -209,7 +215,7 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
 
 def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                   write_back: bool = False, device_control: bool = False,
-                  placement: str = "auto"):
+                  placement: str = "auto", arena_slack: int = 0):
     """The 10,000-tensor group with all N owners on this GPU, as the bench runs
     it: rank 0's gradient arrives as one separate device tensor per parameter
     (10,000 allocations) and is copied into rank 0's flat buffer bucket by
@@ -236,7 +242,7 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                       scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window,
                       windows=windows, fused=fused, own_ranks=True, world=wl.world,
                       arena=arena, min_gap=min_gap, device_control=device_control,
-                      placement=placement)
+                      placement=placement, arena_slack=arena_slack)
     shard.load_param16(I.device_param16(wl, offs, 0, padded, out=shard.param16))
     for r, buf in enumerate(shard.rank_bufs):
         I.device_rank_grad(wl, 1, wl.scale0, r, 0, padded, padded, out=buf)
@@ -270,7 +276,8 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
 
 
 def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fused: bool = True,
-                      device_control: bool = False, placement: str = "auto"):
+                      device_control: bool = False, placement: str = "auto",
+                      arena_slack: int = 0):
     """Round-robin inter-tensor ownership (ZeRO 优化器, "参数分配策略"): this
     owner holds the whole tensors i with i mod N == owner, packed back to back
     (state only for what it owns); each tensor is reduced to it on its own
@@ -298,7 +305,8 @@ def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fuse
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
                       window=wl.window, windows=windows, fused=fused, own_ranks=True,
                       world=wl.world, arena=arena, min_gap=min_gap,
-                      device_control=device_control, placement=placement)
+                      device_control=device_control, placement=placement,
+                      arena_slack=arena_slack)
     for k, i in enumerate(owned):
         a, b = packed[k], packed[k + 1]
         g0 = int(offs[i])
@@ -355,11 +363,13 @@ def main():
     copy_in = None
     write_back = None
     rr_info = None
+    slack = int(args.arena_slack_gib * 2 ** 30)
     if args.round_robin_owner is not None:
         shard, count_rr, n_owned, imbalance = build_round_robin(
             wl, args.round_robin_owner, arena=not args.no_arena,
             min_gap=int(args.min_gap_gib * 2 ** 30), fused=not args.unfused,
-            device_control=not args.host_control, placement=args.placement)
+            device_control=not args.host_control, placement=args.placement,
+            arena_slack=slack)
         begin, end, padded, in_place = 0, count_rr, 0, False
         rr_info = {"owner": args.round_robin_owner, "owned_tensors": n_owned,
                    "owned_elems": count_rr, "largest_over_mean_owner": round(imbalance, 4)}
@@ -367,12 +377,13 @@ def main():
         shard, copy_in, padded, write_back = build_buckets(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
             fused=not args.unfused, write_back=args.write_back,
-            device_control=not args.host_control, placement=args.placement)
+            device_control=not args.host_control, placement=args.placement, arena_slack=slack)
         begin, end, in_place = 0, padded, False
     else:
         shard, begin, end, padded, in_place = build_shard(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
-            fused=not args.unfused, device_control=not args.host_control, placement=args.placement)
+            fused=not args.unfused, device_control=not args.host_control, placement=args.placement,
+            arena_slack=slack)
     count = end - begin
     bufs = shard.rank_bufs
 
@@ -559,6 +570,7 @@ def main():
                              if args.placement == "auto" else "")
                           + f", min gap {args.min_gap_gib:g} GiB"),
             "placement_setup_ms": shard.placement_ms or None,
+            "arena_slack_gib": round(getattr(shard, "arena_slack", 0) / 2 ** 30, 3),
             "parallelism": "one owner partition on one GPU (N ranks simulated in HBM)",
         },
         "step_GBps": round(step_bytes / (whole_ms * 1e-3) / 1e9, 1),

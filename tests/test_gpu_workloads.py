@@ -50,7 +50,7 @@ def _setup(wl, owner_ids, round_robin=False):
 
 
 def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=False,
-               device_control=False, placement=None, in_place_rank=None):
+               device_control=False, placement=None, in_place_rank=None, arena_slack=0):
     """placement: None for separate rank buffers handed to each step, else
     the arena order of a step that holds its own rank buffers."""
     wl = W.WORKLOADS[name]
@@ -62,7 +62,8 @@ def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=F
                       scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window, windows=windows,
                       fused=fused, device_control=device_control, own_ranks=arena,
                       world=wl.world if arena else 0, arena=arena,
-                      placement=placement or "interleaved", in_place_rank=in_place_rank)
+                      placement=placement or "interleaved", in_place_rank=in_place_rank,
+                      arena_slack=arena_slack)
     # initial state: device generator on the GPU, host generator for the oracle
     d_p16 = I.device_param16(wl, offs, begin, end)
     h_p16 = I.host_param16(wl, offs, begin, end, threads)
@@ -152,6 +153,17 @@ def test_arena_orders_parity(placement, in_place_rank):
         assert shard.placement == min(shard.placement_ms, key=shard.placement_ms.get)
     else:
         assert shard.placement == placement and not shard.placement_ms
+
+
+def test_arena_slack_parity():
+    """With slack every order is also tried shifted to the arena's end; the
+    chosen one (either) gives the oracle's results."""
+    shard, _, _, _ = run_parity("toy", [1], steps=3, placement="auto", in_place_rank=3,
+                                arena_slack=1 << 30)
+    assert shard.arena_slack == 1 << 30
+    assert len(shard.placement_ms) == 2 * len(ARENA_ORDERS)
+    assert shard.placement in shard.placement_ms
+    assert shard.arena.numel() >= shard.arena_slack + 4 * shard.count
 
 
 def test_arena_auto_buckets_all_owners():
