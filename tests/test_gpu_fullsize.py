@@ -130,8 +130,11 @@ class SampledOracle:
         return u
 
 
+@pytest.mark.parametrize("device_control", [True, False], ids=["device-control", "host-control"])
 @pytest.mark.parametrize("name", ["llama7b", "llama70b"])
-def test_llama_shard_fullsize_sampled(name):
+def test_llama_shard_fullsize_sampled(name, device_control):
+    """device_control=True is the bench's default launch configuration (the
+    *_ctl calls and the control update); False the host loss scaler."""
     wl = W.WORKLOADS[name]
     offs, parts, padded = oracle.layout(wl.numels, wl.world, wl.align)
     begin, end = int(parts[0]), int(parts[1])
@@ -143,7 +146,8 @@ def test_llama_shard_fullsize_sampled(name):
         pytest.skip(f"{name}: needs {need / 1e9:.1f} GB of device memory, {free / 1e9:.1f} GB free")
     t0 = time.time()
     print(f"{name}: {count} owned elements, {wl.world} ranks, in_place={in_place}", flush=True)
-    shard, _, _, _, _ = bench.build_shard(wl)        # exactly as bench.py runs it
+    # as bench.py runs it (measured placement; its arena slack moves buffers only)
+    shard, _, _, _, _ = bench.build_shard(wl, device_control=device_control)
     bufs = shard.rank_bufs
     flag_o, sumsq_o = host_full_check(wl, begin, end, padded, 1, wl.scale0)
     print(f"{name}: oracle full-shard norm {math.sqrt(sumsq_o):.9g} ({time.time() - t0:.1f} s)",
