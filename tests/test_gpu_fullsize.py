@@ -175,7 +175,10 @@ def test_llama_shard_fullsize_sampled(name, device_control):
         _free_device_memory()
 
 
-def test_buckets_fullsize_all_owners_sampled():
+@pytest.mark.parametrize("device_control", [True, False], ids=["device-control", "host-control"])
+def test_buckets_fullsize_all_owners_sampled(device_control):
+    """device_control=True: the loss scaler, its halvings and the step count
+    advance on the device (the bench's default); False: on the host."""
     wl = W.WORKLOADS["buckets"]
     offs, parts, padded = oracle.layout(wl.numels, wl.world, wl.align)
     first = oracle.buckets(wl.numels, wl.bucket_cap)
@@ -195,7 +198,7 @@ def test_buckets_fullsize_all_owners_sampled():
     shard = ShardStep(0, padded, owners, wl.dtype, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
                       eps=wl.eps, weight_decay=wl.weight_decay, max_grad_norm=wl.clip,
                       scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window,
-                      windows=windows)
+                      windows=windows, device_control=device_control)
     shard.load_param16(I.device_param16(wl, offs, 0, padded, out=shard.param16))
     bufs = [torch.empty(padded, dtype=shard.tdtype, device="cuda") for _ in range(wl.world)]
     extra = [p for p, _ in owners[1:]] + [a for a, _ in windows[1:]] + [v[1] for v in inj.values()]
