@@ -89,11 +89,11 @@ def parse():
                              "streams_first", "ranks_first"],
                     help="order of the buffers in the arena; auto times every order once at "
                          "setup (outside the timed steps) and keeps the fastest")
-    ap.add_argument("--arena-slack-gib", type=float, default=20.0,
+    ap.add_argument("--arena-slack-gib", type=float, default=64.0,
                     help="allocate the arena up to this much larger (never more than is free, "
-                         "less 4 GiB) and let --placement auto also try every order shifted by "
-                         "it, i.e. at other physical addresses; 0 = an arena of exactly the "
-                         "working set")
+                         "less 4 GiB) and let --placement auto also try every order at base "
+                         "offsets 4 GiB apart inside it, i.e. at other physical addresses; 0 = "
+                         "an arena of exactly the working set")
     ap.add_argument("--min-gap-gib", type=float, default=0.0,
                     help="minimum distance between the AdamW streams' bases in the arena")
     ap.add_argument("--flush-gib", type=float, default=0.0,
@@ -364,6 +364,10 @@ def main():
     write_back = None
     rr_info = None
     slack = int(args.arena_slack_gib * 2 ** 30)
+    flush = None
+    if args.flush_gib > 0:
+        # allocated before the shard: the arena's slack is clamped to what is left
+        flush = torch.empty(int(args.flush_gib * 2 ** 30) // 4, dtype=torch.float32, device="cuda")
     if args.round_robin_owner is not None:
         shard, count_rr, n_owned, imbalance = build_round_robin(
             wl, args.round_robin_owner, arena=not args.no_arena,
@@ -428,9 +432,6 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
-    flush = None
-    if args.flush_gib > 0:
-        flush = torch.empty(int(args.flush_gib * 2 ** 30) // 4, dtype=torch.float32, device="cuda")
     injections = 0
     for k in range(args.steps):
         Z.zero_partition_layout(wl.numels, wl.world, wl.align)
@@ -569,7 +570,10 @@ def main():
                           + (" (fastest of the orders timed at setup)"
                              if args.placement == "auto" else "")
                           + f", min gap {args.min_gap_gib:g} GiB"),
-            "placement_setup_ms": shard.placement_ms or None,
+            "placement_candidates": len(shard.placement_ms) or None,
+            "placement_setup_ms": (dict(sorted(shard.placement_ms.items(),
+                                               key=lambda kv: kv[1])[:6])
+                                   if shard.placement_ms else None),
             "arena_slack_gib": round(getattr(shard, "arena_slack", 0) / 2 ** 30, 3),
             "parallelism": "one owner partition on one GPU (N ranks simulated in HBM)",
         },

@@ -36,16 +36,16 @@ allocation, in one of the orders of ARENA_ORDERS (`placement`):
 previous one.  On MI355X the HBM bandwidth of both passes depends on where
 the arrays sit in physical memory, which a process cannot see: the same
 buffers at the same offsets run at different rates in arenas of different
-sizes, and the same rank buffers of the LLaMA-70B shard reduce at 6.1 to
-6.5 TB/s depending on where their block starts.  With placement="auto" the
-step therefore measures: it zeroes the arena, times two steps of the real
-call sequence in every order, three more for the two fastest, and keeps the
-fastest (`placement_ms` holds the times).  That costs three steps per order
-and six more at construction, and no memory beyond the arena.  With
-`arena_slack` bytes (at most what the device has free, less 4 GiB) the arena
-is that much larger and every order is also tried shifted to the arena's
-end: the buffers then sit at other physical addresses (on MI355X 20 GiB of
-slack lets the LLaMA-70B shard's step run 62.4 ms instead of 63.2 ms).
+sizes, and shifting the LLaMA-7B shard's whole layout by 4 GiB steps moves
+its step between 5.9 and 6.4 ms.  With placement="auto" the step therefore
+measures: it zeroes the arena, times one step of the real call sequence in
+every candidate placement, then three more for each of the six fastest,
+and keeps the one with the shortest median of those three (`placement_ms`
+holds the times).  The candidates are the orders of
+ARENA_ORDERS at the arena's start and, with `arena_slack` bytes (at most
+what the device has free, less 4 GiB; the arena is that much larger), at
+every PLACEMENT_STEP into the slack and at its end.  The cost is two steps
+per candidate and 24 more at construction; the slack holds nothing.
 
 Nothing here computes on the data; it sequences calls and keeps host scalars.
 """
@@ -102,6 +102,10 @@ def _ranks_first(names, streams, in_place):
     """The rank buffers, then the AdamW arrays."""
     return _rank_names(names) + [nm for nm in names if not nm.startswith("rank")]
 
+
+# Spacing of the base offsets at which a measured placement tries each
+# order inside the arena's slack.
+PLACEMENT_STEP = 4 << 30
 
 # Buffer orders an arena can be laid out in (see the module docstring).
 ARENA_ORDERS = {
@@ -210,10 +214,14 @@ class ShardStep:
             slack = max(0, min(int(slack), free - size - (4 << 30))) // align * align
         self.arena_slack = slack
         if slack > 0:
+            # every order also at bases every PLACEMENT_STEP bytes into the
+            # slack, and at its end
+            bases = list(range(PLACEMENT_STEP, slack, PLACEMENT_STEP)) + [slack]
             for name in list(plans):
                 offs, end = plans[name]
-                plans[f"{name}@+{slack / 2 ** 30:g}GiB"] = (
-                    {k: v + slack for k, v in offs.items()}, end + slack)
+                for b in bases:
+                    plans[f"{name}@+{b / 2 ** 30:g}GiB"] = (
+                        {k: v + b for k, v in offs.items()}, end + b)
         self.arena = torch.empty(max(size + slack, 1), dtype=torch.uint8, device=device)
         if len(plans) == 1 or n_ranks == 0:
             best = next(iter(plans))
@@ -251,24 +259,29 @@ class ShardStep:
 
     def _tune(self, plans, kinds, n) -> str:
         """Times the step's own calls (reduce windows, check, AdamW per owner)
-        in every order on a zeroed arena and returns the fastest.  Zero
-        gradients raise no overflow, so every pass runs whole.  (On MI355X a
-        zeroed arena runs the step 0.5-1 % faster than gradient data, in
-        every order alike: the choice is the same.)"""
+        in every candidate placement on a zeroed arena and returns the
+        fastest: one warm-up and one timed step each, then three more for
+        the four fastest.  Zero gradients raise no overflow, so every pass
+        runs whole.  (On MI355X a zeroed arena runs the step 0.5-1 % faster
+        than gradient data, in every placement alike: the choice is the
+        same.)"""
         self.arena.zero_()
         for name, (offs, _) in plans.items():
             self._set_views(self._carve(offs, kinds, n))
             self.launch()
-            self.placement_ms[name] = self._time_steps(2)
-        # the two fastest again, three more steps each: close calls are
-        # decided by more than two samples
-        for name in sorted(self.placement_ms, key=self.placement_ms.get)[:2]:
+            self.placement_ms[name] = self._time_steps(1)
+        # the shortest of many single samples is biased low: the finalists are
+        # compared by the median of three fresh steps each
+        finals = {}
+        for name in sorted(self.placement_ms, key=self.placement_ms.get)[:6]:
             self._set_views(self._carve(plans[name][0], kinds, n))
-            self.placement_ms[name] = min(self.placement_ms[name], self._time_steps(3))
-        return min(self.placement_ms, key=self.placement_ms.get)
+            self.launch()
+            finals[name] = self._time_steps(3, median=True)
+            self.placement_ms[name] = finals[name]
+        return min(finals, key=finals.get)
 
-    def _time_steps(self, k: int) -> float:
-        """Shortest of k timed launches of the step's calls (ms)."""
+    def _time_steps(self, k: int, median: bool = False) -> float:
+        """Shortest (or median) of k timed launches of the step's calls (ms)."""
         times = []
         for _ in range(k):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -277,7 +290,7 @@ class ShardStep:
             b.record()
             b.synchronize()
             times.append(a.elapsed_time(b))
-        return round(min(times), 4)
+        return round(float(np.median(times)) if median else min(times), 4)
 
     # ---------------------------------------------------------------- state
     def load_param16(self, param16: torch.Tensor) -> None:
