@@ -229,6 +229,30 @@ __device__ __forceinline__ void flat_copy(uint16_t* flat, const Split& s,
             q[t] = (uintptr_t)(cur.ptr + j0);
             next_ok[t] = lane != 63 && j0 + 2 * kVec <= cur.numel && i + 1 < s.nvec;
             prev_ok[t] = lane != 0 && j0 >= kVec;
+        } else if (vec_lane) {
+            // a vector tile across a tensor boundary or over a gap: its flat
+            // side is one aligned 16-byte chunk, so the tensor side goes
+            // element by element with all loads before the stores (a load and
+            // a store per element would serialise 8 memory round trips, the
+            // two sides may alias)
+            if (GATHER) {
+                uint16_t h[kVec];
+#pragma unroll
+                for (int k = 0; k < kVec; ++k) {
+                    cur.seek(e0[t] + k);
+                    const int64_t j = cur.index(e0[t] + k);
+                    h[k] = j >= 0 ? cur.ptr[j] : (uint16_t)0;
+                }
+                store_nt(flat + e0[t], pack8(h));
+            } else {
+                const u32x4 w = load_nt(flat + e0[t]);
+#pragma unroll
+                for (int k = 0; k < kVec; ++k) {
+                    cur.seek(e0[t] + k);
+                    const int64_t j = cur.index(e0[t] + k);
+                    if (j >= 0) cur.ptr[j] = half_of(w, k);
+                }
+            }
         } else {
             for (int64_t e = e0[t]; e < e0[t] + kVec && e < s.count; ++e) {
                 cur.seek(e);
