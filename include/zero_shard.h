@@ -130,6 +130,13 @@ typedef struct zero_tensor_desc {
     int64_t reserved;   /* set to 0                                               */
 } zero_tensor_desc;
 
+/* A range of elements [offset, offset + count) of the flat buffers a call is
+ * given (for the *_ranges calls).  16 bytes. */
+typedef struct zero_range {
+    int64_t offset;     /* first element, >= 0  */
+    int64_t count;      /* elements, >= 0       */
+} zero_range;
+
 /* ---------------------------------------------------------------- host ---- */
 
 /* Flatten + align + partition (ZeRO-2 source walkthrough, section 4.1 steps
@@ -342,6 +349,45 @@ int zero_adamw_step_ctl(float* master, float* exp_avg, float* exp_avg_sq, void* 
  * Errors: ZERO_EINVAL for NULL pointers. */
 int zero_step_control_update(zero_step_control* ctl, const zero_step_result* res,
                              hipStream_t stream);
+
+/* --------------------------------------------------------- range lists ---- */
+/* One call over several disjoint element ranges of the same buffers: the
+ * ranges an owner holds in one step -- its slice of each reduce bucket
+ * (ZeRO-2 source walkthrough, section 4.2: gradients reduced bucket by bucket
+ * to the partition owners), or, under round-robin ownership (ZeRO optimizer
+ * page, "参数分配策略"), every whole tensor it owns.  The result is that of
+ * the single-range call on each range in list order (zero_reduce_check_owned
+ * with accumulate != 0 after the first, zero_adamw_step per range), except
+ * that sumsq adds the per-block partials of all ranges in one fold, so its
+ * last bits may differ from the chained calls'.  Up to 32 ranges go to one
+ * kernel launch, followed by a single fold of the norm (the chained calls
+ * launch a reduce and a fold per range).
+ *   ranges[n_ranges]  host array, read during the call; offsets and counts
+ *                     >= 0; no element may lie in two ranges (ZERO_EINVAL;
+ *                     ZERO_ERANGE when offset + count overflows int64);
+ *                     empty ranges are allowed and skipped
+ *   ctl               device zero_step_control, or NULL: with ctl the
+ *                     unscale factor, betas and bias corrections come from it
+ *                     (as in the *_ctl calls) and inv_scale / hp->step are
+ *                     ignored
+ * Every other argument as in zero_reduce_check_owned / zero_adamw_step; all
+ * buffers are indexed by the same element offsets. */
+
+/* Bytes of workspace zero_reduce_check_ranges needs for these ranges (0 for
+ * an invalid list). */
+size_t zero_range_workspace_bytes(const zero_range* ranges, int32_t n_ranges);
+
+int zero_reduce_check_ranges(void* dst, const void* const* srcs, int32_t n_ranks,
+                             const zero_range* ranges, int32_t n_ranges, int32_t dtype,
+                             float inv_scale, const zero_step_control* ctl,
+                             zero_step_result* res, void* workspace, size_t workspace_bytes,
+                             int32_t accumulate, hipStream_t stream);
+
+int zero_adamw_step_ranges(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
+                           const void* grad16, const zero_range* ranges, int32_t n_ranges,
+                           int32_t dtype, const zero_adamw_hparams* hp,
+                           const zero_step_control* ctl, const zero_step_result* res,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

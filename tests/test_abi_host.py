@@ -186,3 +186,48 @@ def test_arena_orders_place_every_buffer_once(n_ranks, in_place):
             assert spans[-1][1] == end
             st = sorted(offs[nm] for nm in streams)
             assert all(b - a >= gap for a, b in zip(st, st[1:])), name
+
+
+def test_range_lists_are_checked_before_launching():
+    """The *_ranges calls reject a bad range list on the host, before any
+    launch (no GPU needed): negative offsets or counts, overlapping ranges
+    (ZERO_EINVAL) and offset + count beyond int64 (ZERO_ERANGE).  The
+    workspace bound over a list is the single-range bound's fold of the
+    summed block counts."""
+    import ctypes
+    L = Z.lib()
+    hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1.0, 1)
+    fake = ctypes.c_void_p(0x10000)          # never dereferenced: every call fails first
+    srcs = (ctypes.c_void_p * 2)(fake, fake)
+    bad = {
+        "negative offset": ([(-1, 4)], Z.ZERO_EINVAL),
+        "negative count": ([(0, -4)], Z.ZERO_EINVAL),
+        "overlap": ([(0, 100), (99, 10)], Z.ZERO_EINVAL),
+        "overlap, unsorted": ([(500, 10), (0, 100), (95, 3)], Z.ZERO_EINVAL),
+        "overflow": ([(2 ** 62, 2 ** 62)], Z.ZERO_ERANGE),
+    }
+    for what, (rs, want) in bad.items():
+        arr = Z._ranges(rs)
+        got = L.zero_reduce_check_ranges(fake, srcs, 2, arr, len(rs), Z.ZERO_BF16, 1.0, None, fake,
+                                         fake, 1 << 30, 0, None)
+        assert got == want, what
+        got = L.zero_adamw_step_ranges(fake, fake, fake, fake, fake, arr, len(rs), Z.ZERO_BF16,
+                                       ctypes.byref(hp), None, fake, None)
+        assert got == want, what
+        assert L.zero_range_workspace_bytes(arr, len(rs)) == 0, what
+    # NULL list with entries, NULL result, unknown dtype
+    assert L.zero_reduce_check_ranges(fake, srcs, 2, None, 3, Z.ZERO_BF16, 1.0, None, fake, fake,
+                                      1 << 30, 0, None) == Z.ZERO_EINVAL
+    ok = Z._ranges([(0, 10), (10, 5)])
+    assert L.zero_reduce_check_ranges(fake, srcs, 2, ok, 2, Z.ZERO_BF16, 1.0, None, None, fake,
+                                      1 << 30, 0, None) == Z.ZERO_EINVAL
+    assert L.zero_adamw_step_ranges(fake, fake, fake, fake, fake, ok, 2, 9, ctypes.byref(hp), None,
+                                    fake, None) == Z.ZERO_EINVAL
+    # too small a workspace
+    assert L.zero_reduce_check_ranges(fake, srcs, 2, ok, 2, Z.ZERO_BF16, 1.0, None, fake, fake, 8,
+                                      0, None) == Z.ZERO_EINVAL
+    # workspace bound: one range is the single-range bound; touching ranges are fine
+    assert Z.zero_range_workspace_bytes([(0, 10_000_019)]) == \
+        Z.zero_check_workspace_bytes(10_000_019)
+    assert Z.zero_range_workspace_bytes([(0, 4096), (4096, 4096)]) >= \
+        Z.zero_check_workspace_bytes(8192)

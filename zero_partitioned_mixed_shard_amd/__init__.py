@@ -41,6 +41,10 @@ class zero_loss_scaler(ctypes.Structure):
                 ("skipped", ctypes.c_int64)]
 
 
+class zero_range(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("count", ctypes.c_int64)]
+
+
 class zero_step_control(ctypes.Structure):
     _fields_ = [("scale", ctypes.c_double), ("min_scale", ctypes.c_double),
                 ("window", ctypes.c_int64), ("clean", ctypes.c_int64),
@@ -60,6 +64,7 @@ EXPORTS = (
     "zero_adamw_step", "zero_flat_gather", "zero_flat_scatter",
     "zero_step_control_init", "zero_reduce_check_owned_ctl", "zero_unscale_check_norm_ctl",
     "zero_adamw_step_ctl", "zero_step_control_update",
+    "zero_range_workspace_bytes", "zero_reduce_check_ranges", "zero_adamw_step_ranges",
 )
 
 
@@ -110,6 +115,10 @@ def _load():
                                         ctypes.c_int),
         "zero_adamw_step_ctl": ([P, P, P, P, P, i64, i32, P, P, P, P], ctypes.c_int),
         "zero_step_control_update": ([P, P, P], ctypes.c_int),
+        "zero_range_workspace_bytes": ([P, i32], ctypes.c_size_t),
+        "zero_reduce_check_ranges": ([P, P, i32, P, i32, i32, f32, P, P, P, ctypes.c_size_t, i32, P],
+                                     ctypes.c_int),
+        "zero_adamw_step_ranges": ([P, P, P, P, P, P, i32, i32, P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -406,3 +415,58 @@ def read_result(res) -> zero_step_result:
     """Copy a device zero_step_result to the host (synchronises the stream)."""
     raw = res.detach().cpu().numpy().tobytes()[:RESULT_BYTES]
     return zero_step_result.from_buffer_copy(raw)
+
+
+# ------------------------------------------------------------ range lists ---
+def _ranges(ranges: Sequence) -> "ctypes.Array":
+    """Host array of zero_range from (offset, count) pairs."""
+    arr = (zero_range * max(1, len(ranges)))()
+    for k, (a, c) in enumerate(ranges):
+        arr[k].offset, arr[k].count = int(a), int(c)
+    return arr
+
+
+def zero_range_workspace_bytes(ranges: Sequence) -> int:
+    return int(_lib.zero_range_workspace_bytes(_ranges(ranges), len(ranges)))
+
+
+def _extent(ranges: Sequence) -> int:
+    return max((int(a) + int(c) for a, c in ranges if int(c) > 0), default=0)
+
+
+def zero_reduce_check_ranges(dst, srcs: Sequence, ranges: Sequence, inv_scale: float, res,
+                             workspace, accumulate: bool = False, ctl_dev=None,
+                             stream=None) -> None:
+    """ranges: (offset, count) pairs of elements of dst and every src."""
+    need = _extent(ranges)
+    dt = _dtype_code(dst)
+    if not 1 <= len(srcs) <= ZERO_MAX_RANKS:
+        raise ValueError("1..16 rank buffers")
+    for s in srcs:
+        if _dtype_code(s) != dt:
+            raise TypeError("rank buffers and dst must share the 16-bit type")
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    ptrs = (ctypes.c_void_p * len(srcs))(*[_dev(s, 2, need, "src") for s in srcs])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.zero_reduce_check_ranges(
+        _dev(dst, 2, need, "dst"), ptrs, len(srcs), _ranges(ranges), len(ranges), dt,
+        float(inv_scale), _ctl(ctl_dev) if ctl_dev is not None else None, res.data_ptr(),
+        _dev(workspace, workspace.element_size(), 0, "workspace"), ws_bytes,
+        int(bool(accumulate)), _stream(stream)), "zero_reduce_check_ranges")
+
+
+def zero_adamw_step_ranges(master, exp_avg, exp_avg_sq, param16, grad16, ranges: Sequence,
+                           hp: zero_adamw_hparams, res, ctl_dev=None, stream=None) -> None:
+    need = _extent(ranges)
+    dt = _dtype_code(grad16)
+    if _dtype_code(param16) != dt:
+        raise TypeError("param16 and grad16 must share the 16-bit type")
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    _check(_lib.zero_adamw_step_ranges(
+        _dev(master, 4, need, "master"), _dev(exp_avg, 4, need, "exp_avg"),
+        _dev(exp_avg_sq, 4, need, "exp_avg_sq"), _dev(param16, 2, need, "param16"),
+        _dev(grad16, 2, need, "grad16"), _ranges(ranges), len(ranges), dt, ctypes.byref(hp),
+        _ctl(ctl_dev) if ctl_dev is not None else None, res.data_ptr(), _stream(stream)),
+        "zero_adamw_step_ranges")

@@ -41,6 +41,10 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <utility>
+#include <vector>
+
 #include "zero_common.h"
 
 namespace {
@@ -176,9 +180,9 @@ constexpr int reduce_blocks_per_cu(int nr) { return nr >= 16 ? 1 : (16 / nr > 8 
 // dst may be one of the sources (every element is read, then written, by
 // the same lane).
 template <int DT, int NR, bool CHECK>
-__global__ void __launch_bounds__(kThreads)
-reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, const zero_step_control* ctl,
-              double* part_sum, uint32_t* part_flag) {
+__device__ __forceinline__ void reduce_block(uint16_t* dst, const RankPtrs& src, const Split& s,
+                                             float inv, const zero_step_control* ctl,
+                                             double* part_sum, uint32_t* part_flag) {
     double sq = 0.0;
     uint32_t bad = 0;
     const int64_t blk = block_id(s);
@@ -244,6 +248,46 @@ reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, const zero_step_c
             part_flag[blk] = bad;
         }
     }
+}
+
+template <int DT, int NR, bool CHECK>
+__global__ void __launch_bounds__(kThreads)
+reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, const zero_step_control* ctl,
+              double* part_sum, uint32_t* part_flag) {
+    reduce_block<DT, NR, CHECK>(dst, src, s, inv, ctl, part_sum, part_flag);
+}
+
+// Several disjoint element ranges of the same buffers in one launch.  Range
+// r takes the launch's blocks [first_block[r], first_block[r + 1]) and has
+// its own alignment split, whose blk0 = -first_block[r] makes block_id()
+// range-local; its elements are addressed from offset[r].
+constexpr int kMaxRangesPerLaunch = 32;
+struct RangeTable {
+    int32_t n;
+    int64_t first_block[kMaxRangesPerLaunch + 1];
+    int64_t offset[kMaxRangesPerLaunch];
+    Split split[kMaxRangesPerLaunch];
+};
+
+__device__ __forceinline__ int range_of_block(const RangeTable& tab) {
+    int r = 0;
+    while (r + 1 < tab.n && (int64_t)blockIdx.x >= tab.first_block[r + 1]) ++r;
+    return r;
+}
+
+// One partial per block at part_sum[blockIdx.x] (the host offsets the
+// pointers by the launch's first block among all the call's launches).
+template <int DT, int NR, bool CHECK>
+__global__ void __launch_bounds__(kThreads)
+reduce_ranges_kernel(uint16_t* dst, RankPtrs src, RangeTable tab, float inv,
+                     const zero_step_control* ctl, double* part_sum, uint32_t* part_flag) {
+    const int r = range_of_block(tab);
+    const int64_t off = tab.offset[r];
+    RankPtrs sr = src;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) sr.p[k] = src.p[k] + off;
+    reduce_block<DT, NR, CHECK>(dst + off, sr, tab.split[r], inv, ctl,
+                                part_sum + tab.first_block[r], part_flag + tab.first_block[r]);
 }
 
 // ------------------------------------------------------------- check -------
@@ -434,10 +478,12 @@ __device__ __forceinline__ void adam_quads(const AdamConsts& c0, const zero_step
 // per lane, i.e. two 16-byte fp32 accesses 16 bytes apart that each fill
 // half of every cache line, measured 2% slower on the LLaMA-70B shard.)
 template <int DT>
-__global__ void __launch_bounds__(kThreads)
-adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restrict__ va,
-             uint16_t* __restrict__ p16, const uint16_t* __restrict__ g16, Split s, AdamConsts c0,
-             const zero_step_control* __restrict__ ctl, const zero_step_result* __restrict__ res) {
+__device__ __forceinline__ void adamw_block(float* __restrict__ master, float* __restrict__ ma,
+                                            float* __restrict__ va, uint16_t* __restrict__ p16,
+                                            const uint16_t* __restrict__ g16, const Split& s,
+                                            const AdamConsts& c0,
+                                            const zero_step_control* __restrict__ ctl,
+                                            const zero_step_result* __restrict__ res) {
     if (res->overflow) return;                       // skipped step: write nothing
     if (!s.aligned) {
         const int64_t i = lane_tile(s);
@@ -467,6 +513,25 @@ adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restri
         else if (t >= 64 && t < 64 + kVec && s.head + body + (t - 64) < s.count)
             adam_one<DT>(c, inv, coef, master, ma, va, p16, g16, s.head + body + (t - 64));
     }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads)
+adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restrict__ va,
+             uint16_t* __restrict__ p16, const uint16_t* __restrict__ g16, Split s, AdamConsts c0,
+             const zero_step_control* __restrict__ ctl, const zero_step_result* __restrict__ res) {
+    adamw_block<DT>(master, ma, va, p16, g16, s, c0, ctl, res);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads)
+adamw_ranges_kernel(float* master, float* ma, float* va, uint16_t* p16, const uint16_t* g16,
+                    RangeTable tab, AdamConsts c0, const zero_step_control* __restrict__ ctl,
+                    const zero_step_result* __restrict__ res) {
+    const int r = range_of_block(tab);
+    const int64_t off = tab.offset[r];
+    adamw_block<DT>(master + off, ma + off, va + off, p16 + off, g16 + off, tab.split[r], c0, ctl,
+                    res);
 }
 
 // ------------------------------------------------- device step control ---
@@ -643,14 +708,10 @@ int reduce_check_impl(void* dst, const void* const* srcs, int32_t n_ranks, int64
     return fold_into(ws, L, inv_scale, ctl, accumulate, res, stream);
 }
 
-// AdamW over one partition; the step's betas and bias corrections come from
-// hp (hp->step) or, when ctl is not null, from ctl on the device.
-int adamw_impl(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
-               const void* grad16, int64_t count, int32_t dtype, const zero_adamw_hparams* hp,
-               const zero_step_control* ctl, const zero_step_result* res, hipStream_t stream) {
-    if (count < 0 || !valid_dtype(dtype) || !res) return ZERO_EINVAL;
-    if (count == 0) return ZERO_OK;
-    if (!master || !exp_avg || !exp_avg_sq || !param16 || !grad16) return ZERO_EINVAL;
+// The step's fp32 constants from hp, each rounded once from fp64; with
+// device step control the betas and bias corrections come from ctl instead
+// (read on the device).
+AdamConsts adam_consts(const zero_adamw_hparams* hp, bool ctl) {
     AdamConsts c;
     const double t = ctl ? 1.0 : (double)hp->step;
     c.decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
@@ -663,22 +724,242 @@ int adamw_impl(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
     c.lr = hp->lr;
     c.eps = hp->eps;
     c.max_norm = hp->max_grad_norm;
+    return c;
+}
+
+// 2 resident blocks per CU: 6.10 -> 6.37 TB/s on the LLaMA-70B-shaped shard,
+// 5.33 -> 5.84 TB/s on the 7B one (MI355X)
+constexpr int kAdamBlocksPerCU = 2;
+
+template <int DT>
+int launch_adamw(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* p16,
+                 const uint16_t* g16, const Split& s, const AdamConsts& c,
+                 const zero_step_control* ctl, const zero_step_result* res, hipStream_t stream) {
+    return launch_pieces(s, tile_blocks(s), [&](const Split& piece, int64_t grid) {
+        return launch(adamw_kernel<DT>, grid, lds_for_blocks(kAdamBlocksPerCU), stream, master,
+                      exp_avg, exp_avg_sq, p16, g16, piece, c, ctl, res);
+    });
+}
+
+// AdamW over one partition; the step's betas and bias corrections come from
+// hp (hp->step) or, when ctl is not null, from ctl on the device.
+int adamw_impl(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
+               const void* grad16, int64_t count, int32_t dtype, const zero_adamw_hparams* hp,
+               const zero_step_control* ctl, const zero_step_result* res, hipStream_t stream) {
+    if (count < 0 || !valid_dtype(dtype) || !res) return ZERO_EINVAL;
+    if (count == 0) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !param16 || !grad16) return ZERO_EINVAL;
+    const AdamConsts c = adam_consts(hp, ctl != nullptr);
     const void* p16s[2] = {param16, grad16};
     const void* p32s[3] = {master, exp_avg, exp_avg_sq};
     const Split s = split_for(vector_head(p16s, 2, p32s, 3), count);
-    const int64_t blocks = tile_blocks(s);
     uint16_t* p16 = (uint16_t*)param16;
     const uint16_t* g16 = (const uint16_t*)grad16;
-    // 2 resident blocks per CU: 6.10 -> 6.37 TB/s on the LLaMA-70B-shaped
-    // shard, 5.33 -> 5.84 TB/s on the 7B one (MI355X)
-    const unsigned lds = lds_for_blocks(2);
-    return launch_pieces(s, blocks, [&](const Split& piece, int64_t grid) {
-        return dtype == ZERO_FP16
-                   ? launch(adamw_kernel<ZERO_FP16>, grid, lds, stream, master, exp_avg,
-                            exp_avg_sq, p16, g16, piece, c, ctl, res)
-                   : launch(adamw_kernel<ZERO_BF16>, grid, lds, stream, master, exp_avg,
-                            exp_avg_sq, p16, g16, piece, c, ctl, res);
-    });
+    return dtype == ZERO_FP16
+               ? launch_adamw<ZERO_FP16>(master, exp_avg, exp_avg_sq, p16, g16, s, c, ctl, res, stream)
+               : launch_adamw<ZERO_BF16>(master, exp_avg, exp_avg_sq, p16, g16, s, c, ctl, res, stream);
+}
+
+// ------------------------------------------------------------- ranges -----
+// A list of element ranges: offsets and counts >= 0, offset + count without
+// int64 overflow, and no element in two ranges (empty ranges may sit
+// anywhere).
+int check_ranges(const zero_range* ranges, int32_t n, bool* any_elements) {
+    *any_elements = false;
+    if (n < 0 || (n > 0 && !ranges)) return ZERO_EINVAL;
+    std::vector<std::pair<int64_t, int64_t>> v;
+    v.reserve((size_t)n);
+    for (int32_t r = 0; r < n; ++r) {
+        const int64_t a = ranges[r].offset, c = ranges[r].count;
+        if (a < 0 || c < 0) return ZERO_EINVAL;
+        int64_t end;
+        if (__builtin_add_overflow(a, c, &end)) return ZERO_ERANGE;
+        if (c > 0) v.emplace_back(a, end);
+    }
+    std::sort(v.begin(), v.end());
+    for (size_t k = 1; k < v.size(); ++k)
+        if (v[k].first < v[k - 1].second) return ZERO_EINVAL;
+    *any_elements = !v.empty();
+    return ZERO_OK;
+}
+
+// Runs one call over a list of ranges: the ranges' blocks are numbered one
+// after the other in list order (so per-block partials land in one array),
+// up to kMaxRangesPerLaunch ranges go to one launch of the ranges kernel
+// (go_table), and a range longer than one launch's grid goes alone in
+// pieces (go_single, its Split's blk0 counted from the range's first block).
+template <typename GoTable, typename GoSingle>
+int run_ranges(const zero_range* ranges, int32_t n, const std::vector<Split>& splits,
+               const std::vector<int64_t>& blocks, GoTable&& go_table, GoSingle&& go_single) {
+    RangeTable tab;
+    tab.n = 0;
+    int64_t tab_blocks = 0, base = 0;
+    auto flush = [&]() -> int {
+        if (tab.n == 0) return ZERO_OK;
+        tab.first_block[tab.n] = tab_blocks;
+        const int rc = go_table(tab, tab_blocks, base);
+        base += tab_blocks;
+        tab.n = 0;
+        tab_blocks = 0;
+        return rc;
+    };
+    for (int32_t r = 0; r < n; ++r) {
+        int rc;
+        if (blocks[r] > kMaxLaunchBlocks) {
+            if ((rc = flush()) != ZERO_OK) return rc;
+            if ((rc = go_single(ranges[r].offset, splits[r], blocks[r], base)) != ZERO_OK) return rc;
+            base += blocks[r];
+            continue;
+        }
+        if (tab.n == kMaxRangesPerLaunch || tab_blocks + blocks[r] > kMaxLaunchBlocks)
+            if ((rc = flush()) != ZERO_OK) return rc;
+        Split sp = splits[r];
+        sp.blk0 = -tab_blocks;                         // block_id() range-local
+        tab.first_block[tab.n] = tab_blocks;
+        tab.offset[tab.n] = ranges[r].offset;
+        tab.split[tab.n] = sp;
+        tab.n += 1;
+        tab_blocks += blocks[r];
+    }
+    return flush();
+}
+
+int64_t ranges_max_blocks(const zero_range* ranges, int32_t n) {
+    int64_t b = 0;
+    for (int32_t r = 0; r < n; ++r) b += max_tile_blocks(ranges[r].count > 0 ? ranges[r].count : 0);
+    return b;
+}
+
+template <int DT>
+int reduce_check_ranges_t(uint16_t* dst, const RankPtrs& rp, int32_t n_ranks,
+                          const zero_range* ranges, int32_t n, float inv,
+                          const zero_step_control* ctl, double* ps, uint32_t* pf,
+                          const std::vector<Split>& splits, const std::vector<int64_t>& blocks,
+                          hipStream_t stream) {
+    auto go_table = [&](const RangeTable& tab, int64_t grid, int64_t base) -> int {
+#define ZERO_RANGES_CASE(K)                                                                     \
+    case K:                                                                                     \
+        return launch(reduce_ranges_kernel<DT, K, true>, grid,                                  \
+                      lds_for_blocks(reduce_blocks_per_cu(K)), stream, dst, rp, tab, inv, ctl,  \
+                      ps + base, pf + base);
+        switch (n_ranks) {
+            ZERO_RANGES_CASE(1) ZERO_RANGES_CASE(2) ZERO_RANGES_CASE(3) ZERO_RANGES_CASE(4)
+            ZERO_RANGES_CASE(5) ZERO_RANGES_CASE(6) ZERO_RANGES_CASE(7) ZERO_RANGES_CASE(8)
+            ZERO_RANGES_CASE(9) ZERO_RANGES_CASE(10) ZERO_RANGES_CASE(11) ZERO_RANGES_CASE(12)
+            ZERO_RANGES_CASE(13) ZERO_RANGES_CASE(14) ZERO_RANGES_CASE(15) ZERO_RANGES_CASE(16)
+            default: return ZERO_EINVAL;
+        }
+#undef ZERO_RANGES_CASE
+    };
+    auto go_single = [&](int64_t off, const Split& sp, int64_t, int64_t base) -> int {
+        RankPtrs sr = rp;
+        for (int k = 0; k < n_ranks; ++k) sr.p[k] = rp.p[k] + off;
+        return launch_reduce_n<DT, true>(dst + off, sr, n_ranks, sp, inv, ctl, ps + base, pf + base,
+                                         stream);
+    };
+    return run_ranges(ranges, n, splits, blocks, go_table, go_single);
+}
+
+int reduce_check_ranges_impl(void* dst, const void* const* srcs, int32_t n_ranks,
+                             const zero_range* ranges, int32_t n, int32_t dtype, float inv_scale,
+                             const zero_step_control* ctl, zero_step_result* res, void* workspace,
+                             size_t workspace_bytes, int32_t accumulate, hipStream_t stream) {
+    if (n_ranks < 1 || n_ranks > ZERO_MAX_RANKS || !valid_dtype(dtype) || !srcs) return ZERO_EINVAL;
+    bool any = false;
+    int rc = check_ranges(ranges, n, &any);
+    if (rc != ZERO_OK) return rc;
+    if (any && !dst) return ZERO_EINVAL;
+    RankPtrs rp;
+    for (int r = 0; r < ZERO_MAX_RANKS; ++r) rp.p[r] = nullptr;
+    for (int r = 0; r < n_ranks; ++r) {
+        if (any && !srcs[r]) return ZERO_EINVAL;
+        rp.p[r] = (const uint16_t*)srcs[r];
+    }
+    if (!res || !workspace || ((uintptr_t)workspace & 7) != 0) return ZERO_EINVAL;
+    if (!(inv_scale > 0.0f) || !__builtin_isfinite(inv_scale)) return ZERO_EINVAL;
+    if (workspace_bytes < levels_for(ranges_max_blocks(ranges, n)).bytes) return ZERO_EINVAL;
+    // empty ranges take no blocks: they are dropped here (with no elements
+    // at all only the result is written, or left as it is when accumulating)
+    std::vector<zero_range> rs;
+    std::vector<Split> splits;
+    std::vector<int64_t> blocks;
+    int64_t total = 0;
+    uint16_t* d = (uint16_t*)dst;
+    for (int32_t r = 0; r < n; ++r) {
+        if (ranges[r].count == 0) continue;
+        const int64_t off = ranges[r].offset;
+        const void* all16[ZERO_MAX_RANKS + 1];
+        for (int k = 0; k < n_ranks; ++k) all16[k] = rp.p[k] + off;
+        all16[n_ranks] = d + off;
+        rs.push_back(ranges[r]);
+        splits.push_back(split_for(vector_head(all16, n_ranks + 1, nullptr, 0), ranges[r].count));
+        blocks.push_back(tile_blocks(splits.back(), kReduceTiles));
+        total += blocks.back();
+    }
+    const int32_t m = (int32_t)rs.size();
+    const Levels L = levels_for(total);
+    char* ws = (char*)workspace;
+    double* ps = (double*)(ws + L.sum_off[0]);
+    uint32_t* pf = (uint32_t*)(ws + L.flag_off[0]);
+    rc = dtype == ZERO_FP16
+             ? reduce_check_ranges_t<ZERO_FP16>(d, rp, n_ranks, rs.data(), m, inv_scale, ctl, ps,
+                                                pf, splits, blocks, stream)
+             : reduce_check_ranges_t<ZERO_BF16>(d, rp, n_ranks, rs.data(), m, inv_scale, ctl, ps,
+                                                pf, splits, blocks, stream);
+    if (rc != ZERO_OK) return rc;
+    return fold_into(ws, L, inv_scale, ctl, accumulate, res, stream);
+}
+
+template <int DT>
+int adamw_ranges_t(float* master, float* ma, float* va, uint16_t* p16, const uint16_t* g16,
+                   const zero_range* ranges, int32_t n, const AdamConsts& c,
+                   const zero_step_control* ctl, const zero_step_result* res,
+                   const std::vector<Split>& splits, const std::vector<int64_t>& blocks,
+                   hipStream_t stream) {
+    auto go_table = [&](const RangeTable& tab, int64_t grid, int64_t) -> int {
+        return launch(adamw_ranges_kernel<DT>, grid, lds_for_blocks(kAdamBlocksPerCU), stream,
+                      master, ma, va, p16, g16, tab, c, ctl, res);
+    };
+    auto go_single = [&](int64_t off, const Split& sp, int64_t, int64_t) -> int {
+        return launch_adamw<DT>(master + off, ma + off, va + off, p16 + off, g16 + off, sp, c, ctl,
+                                res, stream);
+    };
+    return run_ranges(ranges, n, splits, blocks, go_table, go_single);
+}
+
+int adamw_ranges_impl(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
+                      const void* grad16, const zero_range* ranges, int32_t n, int32_t dtype,
+                      const zero_adamw_hparams* hp, const zero_step_control* ctl,
+                      const zero_step_result* res, hipStream_t stream) {
+    if (!valid_dtype(dtype) || !res || !hp) return ZERO_EINVAL;
+    if (!ctl && hp->step < 1) return ZERO_EINVAL;
+    bool any = false;
+    const int rc = check_ranges(ranges, n, &any);
+    if (rc != ZERO_OK) return rc;
+    if (!any) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !param16 || !grad16) return ZERO_EINVAL;
+    const AdamConsts c = adam_consts(hp, ctl != nullptr);
+    uint16_t* p16 = (uint16_t*)param16;
+    const uint16_t* g16 = (const uint16_t*)grad16;
+    // empty ranges take no blocks: they are dropped here
+    std::vector<zero_range> rs;
+    std::vector<Split> splits;
+    std::vector<int64_t> blocks;
+    for (int32_t r = 0; r < n; ++r) {
+        if (ranges[r].count == 0) continue;
+        const int64_t off = ranges[r].offset;
+        const void* p16s[2] = {p16 + off, g16 + off};
+        const void* p32s[3] = {master + off, exp_avg + off, exp_avg_sq + off};
+        rs.push_back(ranges[r]);
+        splits.push_back(split_for(vector_head(p16s, 2, p32s, 3), ranges[r].count));
+        blocks.push_back(tile_blocks(splits.back()));
+    }
+    const int32_t m = (int32_t)rs.size();
+    return dtype == ZERO_FP16
+               ? adamw_ranges_t<ZERO_FP16>(master, exp_avg, exp_avg_sq, p16, g16, rs.data(), m, c,
+                                           ctl, res, splits, blocks, stream)
+               : adamw_ranges_t<ZERO_BF16>(master, exp_avg, exp_avg_sq, p16, g16, rs.data(), m, c,
+                                           ctl, res, splits, blocks, stream);
 }
 
 }  // namespace
@@ -860,6 +1141,31 @@ int zero_adamw_step_ctl(float* master, float* exp_avg, float* exp_avg_sq, void* 
     if (!hp || !ctl) return ZERO_EINVAL;
     return adamw_impl(master, exp_avg, exp_avg_sq, param16, grad16, count, dtype, hp, ctl, res,
                       stream);
+}
+
+size_t zero_range_workspace_bytes(const zero_range* ranges, int32_t n_ranges) {
+    bool any = false;
+    if (check_ranges(ranges, n_ranges, &any) != ZERO_OK) return 0;
+    return levels_for(ranges_max_blocks(ranges, n_ranges)).bytes;
+}
+
+int zero_reduce_check_ranges(void* dst, const void* const* srcs, int32_t n_ranks,
+                             const zero_range* ranges, int32_t n_ranges, int32_t dtype,
+                             float inv_scale, const zero_step_control* ctl,
+                             zero_step_result* res, void* workspace, size_t workspace_bytes,
+                             int32_t accumulate, hipStream_t stream) {
+    return reduce_check_ranges_impl(dst, srcs, n_ranks, ranges, n_ranges, dtype,
+                                    ctl ? 1.0f : inv_scale, ctl, res, workspace, workspace_bytes,
+                                    accumulate, stream);
+}
+
+int zero_adamw_step_ranges(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
+                           const void* grad16, const zero_range* ranges, int32_t n_ranges,
+                           int32_t dtype, const zero_adamw_hparams* hp,
+                           const zero_step_control* ctl, const zero_step_result* res,
+                           hipStream_t stream) {
+    return adamw_ranges_impl(master, exp_avg, exp_avg_sq, param16, grad16, ranges, n_ranges,
+                             dtype, hp, ctl, res, stream);
 }
 
 int zero_step_control_init(zero_step_control* ctl, double scale0, double min_scale,
