@@ -105,6 +105,9 @@ def parse():
                          "occurrences) or NaN (even) at a seeded index: the step is skipped "
                          "and the loss scale halves; 0 = off (default 4 for the buckets "
                          "workload, whose protocol has an overflow every 4th step; else 0)")
+    ap.add_argument("--no-batch", action="store_true",
+                    help="one reduce+check call per reduce window and one AdamW call per owner, "
+                         "instead of one range-list call each (bucket group, round-robin owner)")
     ap.add_argument("--host-control", action="store_true",
                     help="keep the loss scaler and step count on the host: every step ends with "
                          "a 16-byte result readback (the GPU idles while the host updates the "
@@ -185,7 +188,8 @@ def cpu_baseline(wl, begin: int, seconds: float) -> dict:
 
 
 def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
-                device_control: bool = False, placement: str = "auto", arena_slack: int = 0):
+                device_control: bool = False, placement: str = "auto", arena_slack: int = 0,
+                batched: bool = True):
     """Owner 0's shard of `wl` as the bench runs it: state, reduced gradient
     and the N rank buffers (the LLaMA-70B shard reduces in place into rank 0's
     buffer), initial 16-bit weights and one gradient batch generated on the
@@ -205,7 +209,7 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                       window=wl.window, in_place_rank=0 if in_place else None, fused=fused,
                       own_ranks=True, world=wl.world, arena=arena, min_gap=min_gap,
                       device_control=device_control, placement=placement,
-                      arena_slack=arena_slack)
+                      arena_slack=arena_slack, batched=batched)
     shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16))
     for r, buf in enumerate(shard.rank_bufs):
         I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded, out=buf)
@@ -215,7 +219,7 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
 
 def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                   write_back: bool = False, device_control: bool = False,
-                  placement: str = "auto", arena_slack: int = 0):
+                  placement: str = "auto", arena_slack: int = 0, batched: bool = True):
     """The 10,000-tensor group with all N owners on this GPU, as the bench runs
     it: rank 0's gradient arrives as one separate device tensor per parameter
     (10,000 allocations) and is copied into rank 0's flat buffer bucket by
@@ -242,7 +246,7 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                       scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window,
                       windows=windows, fused=fused, own_ranks=True, world=wl.world,
                       arena=arena, min_gap=min_gap, device_control=device_control,
-                      placement=placement, arena_slack=arena_slack)
+                      placement=placement, arena_slack=arena_slack, batched=batched)
     shard.load_param16(I.device_param16(wl, offs, 0, padded, out=shard.param16))
     for r, buf in enumerate(shard.rank_bufs):
         I.device_rank_grad(wl, 1, wl.scale0, r, 0, padded, padded, out=buf)
@@ -277,7 +281,7 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
 
 def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fused: bool = True,
                       device_control: bool = False, placement: str = "auto",
-                      arena_slack: int = 0):
+                      arena_slack: int = 0, batched: bool = True):
     """Round-robin inter-tensor ownership (ZeRO 优化器, "参数分配策略"): this
     owner holds the whole tensors i with i mod N == owner, packed back to back
     (state only for what it owns); each tensor is reduced to it on its own
@@ -306,7 +310,7 @@ def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fuse
                       window=wl.window, windows=windows, fused=fused, own_ranks=True,
                       world=wl.world, arena=arena, min_gap=min_gap,
                       device_control=device_control, placement=placement,
-                      arena_slack=arena_slack)
+                      arena_slack=arena_slack, batched=batched)
     for k, i in enumerate(owned):
         a, b = packed[k], packed[k + 1]
         g0 = int(offs[i])
@@ -373,7 +377,7 @@ def main():
             wl, args.round_robin_owner, arena=not args.no_arena,
             min_gap=int(args.min_gap_gib * 2 ** 30), fused=not args.unfused,
             device_control=not args.host_control, placement=args.placement,
-            arena_slack=slack)
+            arena_slack=slack, batched=not args.no_batch)
         begin, end, padded, in_place = 0, count_rr, 0, False
         rr_info = {"owner": args.round_robin_owner, "owned_tensors": n_owned,
                    "owned_elems": count_rr, "largest_over_mean_owner": round(imbalance, 4)}
@@ -381,13 +385,14 @@ def main():
         shard, copy_in, padded, write_back = build_buckets(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
             fused=not args.unfused, write_back=args.write_back,
-            device_control=not args.host_control, placement=args.placement, arena_slack=slack)
+            device_control=not args.host_control, placement=args.placement, arena_slack=slack,
+            batched=not args.no_batch)
         begin, end, in_place = 0, padded, False
     else:
         shard, begin, end, padded, in_place = build_shard(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
             fused=not args.unfused, device_control=not args.host_control, placement=args.placement,
-            arena_slack=slack)
+            arena_slack=slack, batched=not args.no_batch)
     count = end - begin
     bufs = shard.rank_bufs
 
@@ -560,6 +565,7 @@ def main():
             "clip": wl.clip,
             "in_place_reduce": in_place,
             "fused_reduce_check": not args.unfused,
+            "range_list_calls": not args.no_batch,
             "step_control": "host (16-byte readback per step)" if args.host_control else
                             "device-resident (no per-step readback)",
             "graph": bool(args.graph),
@@ -571,9 +577,9 @@ def main():
                              if args.placement == "auto" else "")
                           + f", min gap {args.min_gap_gib:g} GiB"),
             "placement_candidates": len(shard.placement_ms) or None,
-            "placement_setup_ms": (dict(sorted(shard.placement_ms.items(),
-                                               key=lambda kv: kv[1])[:6])
-                                   if shard.placement_ms else None),
+            # the finalists' medians of three timed steps (the choice is their minimum)
+            "placement_setup_ms": dict(sorted(getattr(shard, "placement_finalists_ms", {}).items(),
+                                              key=lambda kv: kv[1])) or None,
             "arena_slack_gib": round(getattr(shard, "arena_slack", 0) / 2 ** 30, 3),
             "parallelism": "one owner partition on one GPU (N ranks simulated in HBM)",
         },

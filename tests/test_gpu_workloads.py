@@ -50,7 +50,8 @@ def _setup(wl, owner_ids, round_robin=False):
 
 
 def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=False,
-               device_control=False, placement=None, in_place_rank=None, arena_slack=0):
+               device_control=False, placement=None, in_place_rank=None, arena_slack=0,
+               batched=True):
     """placement: None for separate rank buffers handed to each step, else
     the arena order of a step that holds its own rank buffers."""
     wl = W.WORKLOADS[name]
@@ -63,7 +64,7 @@ def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=F
                       fused=fused, device_control=device_control, own_ranks=arena,
                       world=wl.world if arena else 0, arena=arena,
                       placement=placement or "interleaved", in_place_rank=in_place_rank,
-                      arena_slack=arena_slack)
+                      arena_slack=arena_slack, batched=batched)
     # initial state: device generator on the GPU, host generator for the oracle
     d_p16 = I.device_param16(wl, offs, begin, end)
     h_p16 = I.host_param16(wl, offs, begin, end, threads)
@@ -122,12 +123,14 @@ def test_bert_owner0_all_steps_clip():
     run_parity("bert", [0])
 
 
-@pytest.mark.parametrize("name,owner", [("toy", 0), ("toy", 5), ("bert", 3)])
-def test_round_robin_ownership(name, owner):
+@pytest.mark.parametrize("name,owner,batched", [("toy", 0, True), ("toy", 5, True),
+                                                ("bert", 3, True), ("bert", 3, False)])
+def test_round_robin_ownership(name, owner, batched):
     """Whole tensors i with i mod N == owner (ZeRO 优化器, "参数分配策略"):
-    one reduce+check call per owned tensor, accumulated into one norm, and one
-    AdamW call per owned tensor."""
-    run_parity(name, [owner], steps=4, round_robin=True)
+    every owned tensor is its own reduce window and AdamW range -- one
+    range-list call each (batched), or one reduce+check call per tensor,
+    accumulated into one norm, and one AdamW call per tensor."""
+    run_parity(name, [owner], steps=4, round_robin=True, batched=batched)
 
 
 def test_round_robin_all_owners_equals_flat_union():
@@ -150,7 +153,9 @@ def test_arena_orders_parity(placement, in_place_rank):
     assert shard.placement in ARENA_ORDERS
     if placement == "auto":
         assert set(shard.placement_ms) == set(ARENA_ORDERS)
-        assert shard.placement == min(shard.placement_ms, key=shard.placement_ms.get)
+        fin = shard.placement_finalists_ms
+        assert len(fin) == min(6, len(ARENA_ORDERS)) and set(fin) <= set(shard.placement_ms)
+        assert shard.placement == min(fin, key=fin.get)
     else:
         assert shard.placement == placement and not shard.placement_ms
 
@@ -174,11 +179,14 @@ def test_arena_auto_buckets_all_owners():
     assert skipped == 2 and t == 6
 
 
-@pytest.mark.parametrize("fused", [True, False])
-def test_buckets_small_all_owners_dynamic_scaling(fused):
-    """Fused: one reduce+check call per bucket-x-owner window.  Unfused:
-    reduce per window, then check per owner."""
-    shard, scaler, skipped, t = run_parity("buckets_small", list(range(16)), fused=fused)
+@pytest.mark.parametrize("fused,batched", [(True, True), (True, False), (False, True)])
+def test_buckets_small_all_owners_dynamic_scaling(fused, batched):
+    """Fused and batched: one range-list reduce+check call over all
+    bucket-x-owner windows and one range-list AdamW over all owners.  Fused,
+    not batched: one reduce+check call per window, accumulated, and one AdamW
+    per owner.  Unfused: reduce per window, then check per owner."""
+    shard, scaler, skipped, t = run_parity("buckets_small", list(range(16)), fused=fused,
+                                           batched=batched)
     # ten inf/NaN injections in 40 steps: ten halvings of 2^16, t = 30
     assert skipped == 10 and t == 30 and scaler.scale == 64.0
 

@@ -257,39 +257,6 @@ reduce_kernel(uint16_t* dst, RankPtrs src, Split s, float inv, const zero_step_c
     reduce_block<DT, NR, CHECK>(dst, src, s, inv, ctl, part_sum, part_flag);
 }
 
-// Several disjoint element ranges of the same buffers in one launch.  Range
-// r takes the launch's blocks [first_block[r], first_block[r + 1]) and has
-// its own alignment split, whose blk0 = -first_block[r] makes block_id()
-// range-local; its elements are addressed from offset[r].
-constexpr int kMaxRangesPerLaunch = 32;
-struct RangeTable {
-    int32_t n;
-    int64_t first_block[kMaxRangesPerLaunch + 1];
-    int64_t offset[kMaxRangesPerLaunch];
-    Split split[kMaxRangesPerLaunch];
-};
-
-__device__ __forceinline__ int range_of_block(const RangeTable& tab) {
-    int r = 0;
-    while (r + 1 < tab.n && (int64_t)blockIdx.x >= tab.first_block[r + 1]) ++r;
-    return r;
-}
-
-// One partial per block at part_sum[blockIdx.x] (the host offsets the
-// pointers by the launch's first block among all the call's launches).
-template <int DT, int NR, bool CHECK>
-__global__ void __launch_bounds__(kThreads)
-reduce_ranges_kernel(uint16_t* dst, RankPtrs src, RangeTable tab, float inv,
-                     const zero_step_control* ctl, double* part_sum, uint32_t* part_flag) {
-    const int r = range_of_block(tab);
-    const int64_t off = tab.offset[r];
-    RankPtrs sr = src;
-#pragma unroll
-    for (int k = 0; k < NR; ++k) sr.p[k] = src.p[k] + off;
-    reduce_block<DT, NR, CHECK>(dst + off, sr, tab.split[r], inv, ctl,
-                                part_sum + tab.first_block[r], part_flag + tab.first_block[r]);
-}
-
 // ------------------------------------------------------------- check -------
 template <int DT>
 __global__ void __launch_bounds__(kThreads)
@@ -521,17 +488,6 @@ adamw_kernel(float* __restrict__ master, float* __restrict__ ma, float* __restri
              uint16_t* __restrict__ p16, const uint16_t* __restrict__ g16, Split s, AdamConsts c0,
              const zero_step_control* __restrict__ ctl, const zero_step_result* __restrict__ res) {
     adamw_block<DT>(master, ma, va, p16, g16, s, c0, ctl, res);
-}
-
-template <int DT>
-__global__ void __launch_bounds__(kThreads)
-adamw_ranges_kernel(float* master, float* ma, float* va, uint16_t* p16, const uint16_t* g16,
-                    RangeTable tab, AdamConsts c0, const zero_step_control* __restrict__ ctl,
-                    const zero_step_result* __restrict__ res) {
-    const int r = range_of_block(tab);
-    const int64_t off = tab.offset[r];
-    adamw_block<DT>(master + off, ma + off, va + off, p16 + off, g16 + off, tab.split[r], c0, ctl,
-                    res);
 }
 
 // ------------------------------------------------- device step control ---
@@ -783,81 +739,35 @@ int check_ranges(const zero_range* ranges, int32_t n, bool* any_elements) {
     return ZERO_OK;
 }
 
-// Runs one call over a list of ranges: the ranges' blocks are numbered one
-// after the other in list order (so per-block partials land in one array),
-// up to kMaxRangesPerLaunch ranges go to one launch of the ranges kernel
-// (go_table), and a range longer than one launch's grid goes alone in
-// pieces (go_single, its Split's blk0 counted from the range's first block).
-template <typename GoTable, typename GoSingle>
-int run_ranges(const zero_range* ranges, int32_t n, const std::vector<Split>& splits,
-               const std::vector<int64_t>& blocks, GoTable&& go_table, GoSingle&& go_single) {
-    RangeTable tab;
-    tab.n = 0;
-    int64_t tab_blocks = 0, base = 0;
-    auto flush = [&]() -> int {
-        if (tab.n == 0) return ZERO_OK;
-        tab.first_block[tab.n] = tab_blocks;
-        const int rc = go_table(tab, tab_blocks, base);
-        base += tab_blocks;
-        tab.n = 0;
-        tab_blocks = 0;
-        return rc;
-    };
-    for (int32_t r = 0; r < n; ++r) {
-        int rc;
-        if (blocks[r] > kMaxLaunchBlocks) {
-            if ((rc = flush()) != ZERO_OK) return rc;
-            if ((rc = go_single(ranges[r].offset, splits[r], blocks[r], base)) != ZERO_OK) return rc;
-            base += blocks[r];
-            continue;
-        }
-        if (tab.n == kMaxRangesPerLaunch || tab_blocks + blocks[r] > kMaxLaunchBlocks)
-            if ((rc = flush()) != ZERO_OK) return rc;
-        Split sp = splits[r];
-        sp.blk0 = -tab_blocks;                         // block_id() range-local
-        tab.first_block[tab.n] = tab_blocks;
-        tab.offset[tab.n] = ranges[r].offset;
-        tab.split[tab.n] = sp;
-        tab.n += 1;
-        tab_blocks += blocks[r];
-    }
-    return flush();
-}
-
 int64_t ranges_max_blocks(const zero_range* ranges, int32_t n) {
     int64_t b = 0;
     for (int32_t r = 0; r < n; ++r) b += max_tile_blocks(ranges[r].count > 0 ? ranges[r].count : 0);
     return b;
 }
 
+// Reduce+check over a list of ranges: each range is one launch of the
+// single-range kernel (in pieces past one grid's size), its block partials
+// written after the previous ranges' (range r's first partial at the sum of
+// the earlier ranges' block counts), so the norm of all ranges is folded
+// once.  (Packing several ranges into one launch made every block look up
+// its range before its first load; the dependent scalar loads cost 2-4 %.)
 template <int DT>
 int reduce_check_ranges_t(uint16_t* dst, const RankPtrs& rp, int32_t n_ranks,
                           const zero_range* ranges, int32_t n, float inv,
                           const zero_step_control* ctl, double* ps, uint32_t* pf,
                           const std::vector<Split>& splits, const std::vector<int64_t>& blocks,
                           hipStream_t stream) {
-    auto go_table = [&](const RangeTable& tab, int64_t grid, int64_t base) -> int {
-#define ZERO_RANGES_CASE(K)                                                                     \
-    case K:                                                                                     \
-        return launch(reduce_ranges_kernel<DT, K, true>, grid,                                  \
-                      lds_for_blocks(reduce_blocks_per_cu(K)), stream, dst, rp, tab, inv, ctl,  \
-                      ps + base, pf + base);
-        switch (n_ranks) {
-            ZERO_RANGES_CASE(1) ZERO_RANGES_CASE(2) ZERO_RANGES_CASE(3) ZERO_RANGES_CASE(4)
-            ZERO_RANGES_CASE(5) ZERO_RANGES_CASE(6) ZERO_RANGES_CASE(7) ZERO_RANGES_CASE(8)
-            ZERO_RANGES_CASE(9) ZERO_RANGES_CASE(10) ZERO_RANGES_CASE(11) ZERO_RANGES_CASE(12)
-            ZERO_RANGES_CASE(13) ZERO_RANGES_CASE(14) ZERO_RANGES_CASE(15) ZERO_RANGES_CASE(16)
-            default: return ZERO_EINVAL;
-        }
-#undef ZERO_RANGES_CASE
-    };
-    auto go_single = [&](int64_t off, const Split& sp, int64_t, int64_t base) -> int {
+    int64_t base = 0;
+    for (int32_t r = 0; r < n; ++r) {
+        const int64_t off = ranges[r].offset;
         RankPtrs sr = rp;
         for (int k = 0; k < n_ranks; ++k) sr.p[k] = rp.p[k] + off;
-        return launch_reduce_n<DT, true>(dst + off, sr, n_ranks, sp, inv, ctl, ps + base, pf + base,
-                                         stream);
-    };
-    return run_ranges(ranges, n, splits, blocks, go_table, go_single);
+        const int rc = launch_reduce_n<DT, true>(dst + off, sr, n_ranks, splits[r], inv, ctl,
+                                                 ps + base, pf + base, stream);
+        if (rc != ZERO_OK) return rc;
+        base += blocks[r];
+    }
+    return ZERO_OK;
 }
 
 int reduce_check_ranges_impl(void* dst, const void* const* srcs, int32_t n_ranks,
@@ -914,17 +824,14 @@ template <int DT>
 int adamw_ranges_t(float* master, float* ma, float* va, uint16_t* p16, const uint16_t* g16,
                    const zero_range* ranges, int32_t n, const AdamConsts& c,
                    const zero_step_control* ctl, const zero_step_result* res,
-                   const std::vector<Split>& splits, const std::vector<int64_t>& blocks,
-                   hipStream_t stream) {
-    auto go_table = [&](const RangeTable& tab, int64_t grid, int64_t) -> int {
-        return launch(adamw_ranges_kernel<DT>, grid, lds_for_blocks(kAdamBlocksPerCU), stream,
-                      master, ma, va, p16, g16, tab, c, ctl, res);
-    };
-    auto go_single = [&](int64_t off, const Split& sp, int64_t, int64_t) -> int {
-        return launch_adamw<DT>(master + off, ma + off, va + off, p16 + off, g16 + off, sp, c, ctl,
-                                res, stream);
-    };
-    return run_ranges(ranges, n, splits, blocks, go_table, go_single);
+                   const std::vector<Split>& splits, hipStream_t stream) {
+    for (int32_t r = 0; r < n; ++r) {
+        const int64_t off = ranges[r].offset;
+        const int rc = launch_adamw<DT>(master + off, ma + off, va + off, p16 + off, g16 + off,
+                                        splits[r], c, ctl, res, stream);
+        if (rc != ZERO_OK) return rc;
+    }
+    return ZERO_OK;
 }
 
 int adamw_ranges_impl(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
@@ -944,7 +851,6 @@ int adamw_ranges_impl(float* master, float* exp_avg, float* exp_avg_sq, void* pa
     // empty ranges take no blocks: they are dropped here
     std::vector<zero_range> rs;
     std::vector<Split> splits;
-    std::vector<int64_t> blocks;
     for (int32_t r = 0; r < n; ++r) {
         if (ranges[r].count == 0) continue;
         const int64_t off = ranges[r].offset;
@@ -952,14 +858,13 @@ int adamw_ranges_impl(float* master, float* exp_avg, float* exp_avg_sq, void* pa
         const void* p32s[3] = {master + off, exp_avg + off, exp_avg_sq + off};
         rs.push_back(ranges[r]);
         splits.push_back(split_for(vector_head(p16s, 2, p32s, 3), ranges[r].count));
-        blocks.push_back(tile_blocks(splits.back()));
     }
     const int32_t m = (int32_t)rs.size();
     return dtype == ZERO_FP16
                ? adamw_ranges_t<ZERO_FP16>(master, exp_avg, exp_avg_sq, p16, g16, rs.data(), m, c,
-                                           ctl, res, splits, blocks, stream)
+                                           ctl, res, splits, stream)
                : adamw_ranges_t<ZERO_BF16>(master, exp_avg, exp_avg_sq, p16, g16, rs.data(), m, c,
-                                           ctl, res, splits, blocks, stream);
+                                           ctl, res, splits, stream);
 }
 
 }  // namespace

@@ -12,6 +12,12 @@ runs one step as the library's calls:
                                             on the device)
   16-byte readback                          zero_loss_scaler_update, t
 
+With several reduce windows or owners (a bucketed group with all owners on
+one GPU, round-robin ownership with one window per owned tensor) the fused
+step makes one range-list call for all windows (zero_reduce_check_ranges)
+and one for all owners (zero_adamw_step_ranges); batched=False keeps one
+call per window and per owner.
+
 With fused=False the reduce and the check are separate calls
 (zero_reduce_owned per window, then zero_unscale_check_norm per owner).
 
@@ -40,8 +46,9 @@ sizes, and shifting the LLaMA-7B shard's whole layout by 4 GiB steps moves
 its step between 5.9 and 6.4 ms.  With placement="auto" the step therefore
 measures: it zeroes the arena, times one step of the real call sequence in
 every candidate placement, then three more for each of the six fastest,
-and keeps the one with the shortest median of those three (`placement_ms`
-holds the times).  The candidates are the orders of
+and keeps the one with the shortest median of those three
+(`placement_ms` holds the first stage's times, `placement_finalists_ms` the
+medians).  The candidates are the orders of
 ARENA_ORDERS at the arena's start and, with `arena_slack` bytes (at most
 what the device has free, less 4 GiB; the arena is that much larger), at
 every PLACEMENT_STEP into the slack and at its end.  The cost is two steps
@@ -62,7 +69,8 @@ from . import (RESULT_BYTES, ZERO_BF16, ZERO_FP16, control_to_device, read_contr
                zero_check_workspace_bytes, zero_init_master, zero_loss_scaler,
                zero_loss_scaler_update, zero_reduce_check_owned, zero_reduce_check_owned_ctl,
                zero_reduce_owned, zero_step_control_init, zero_step_control_update,
-               zero_unscale_check_norm, zero_unscale_check_norm_ctl)
+               zero_unscale_check_norm, zero_unscale_check_norm_ctl, zero_adamw_step_ranges,
+               zero_range_workspace_bytes, zero_reduce_check_ranges)
 
 
 def _interleaved(names, streams, in_place):
@@ -136,7 +144,7 @@ class ShardStep:
                  divisor: int = 1, in_place_rank: Optional[int] = None, fused: bool = True,
                  own_ranks: bool = False, world: int = 0, arena: bool = False,
                  min_gap: int = 0, device_control: bool = False, placement: str = "interleaved",
-                 arena_slack: int = 0, device="cuda"):
+                 arena_slack: int = 0, batched: bool = True, device="cuda"):
         self.begin, self.end = begin, end
         self.count = end - begin
         self.owners = [(a - begin, b - begin) for a, b in owners]
@@ -167,11 +175,19 @@ class ShardStep:
         self.n_ranks = n_ranks
         self.res = torch.zeros(RESULT_BYTES // 4, dtype=torch.int32, device=device)
         self.ctl = None
+        # several reduce windows / owners: one range-list call each instead
+        # of one call per range (fused path)
+        self.batched = batched
+        self._reduce_list = [(a, b - a) for a, b in self.reduce_ranges]
+        self._owner_list = [(a, b - a) for a, b in self.owners]
         spans = [b - a for a, b in self.owners] + [b - a for a, b in self.reduce_ranges]
         ws = max(zero_check_workspace_bytes(n) for n in spans) if spans else 64
+        if batched and len(self._reduce_list) > 1:
+            ws = max(ws, zero_range_workspace_bytes(self._reduce_list))
         self.workspace = torch.empty((ws + 7) // 8, dtype=torch.float64, device=device)
         self.placement = placement if arena else "separate"
-        self.placement_ms = {}
+        self.placement_ms = {}                  # first stage: one timed step per candidate
+        self.placement_finalists_ms = {}        # second stage: median of three, six fastest
         self.arena_slack = 0
         self._allocate(n, n_ranks, in_place_rank is None, arena, min_gap, placement,
                        arena_slack, device)
@@ -277,7 +293,7 @@ class ShardStep:
             self._set_views(self._carve(plans[name][0], kinds, n))
             self.launch()
             finals[name] = self._time_steps(3, median=True)
-            self.placement_ms[name] = finals[name]
+        self.placement_finalists_ms = finals
         return min(finals, key=finals.get)
 
     def _time_steps(self, k: int, median: bool = False) -> float:
@@ -329,7 +345,12 @@ class ShardStep:
         inv = self.inv_scale
         if marks:
             marks[0].record()
-        if self.fused:
+        if self.fused and self.batched and len(self._reduce_list) > 1:
+            zero_reduce_check_ranges(red, rank_bufs, self._reduce_list, inv, self.res,
+                                     self.workspace, ctl_dev=ctl)
+            if marks:
+                marks[1].record()
+        elif self.fused:
             for k, (a, b) in enumerate(self.reduce_ranges):
                 srcs = [r[a:b] for r in rank_bufs]
                 if ctl is None:
@@ -355,13 +376,17 @@ class ShardStep:
         if marks:
             marks[2].record()
         self.hp.step = self.t + 1
-        for a, b in self.owners:
-            args = (self.master[a:b], self.exp_avg[a:b], self.exp_avg_sq[a:b],
-                    self.param16[a:b], red[a:b], self.hp)
-            if ctl is None:
-                zero_adamw_step(*args, self.res)
-            else:
-                zero_adamw_step_ctl(*args, ctl, self.res)
+        if self.batched and len(self._owner_list) > 1:
+            zero_adamw_step_ranges(self.master, self.exp_avg, self.exp_avg_sq, self.param16, red,
+                                   self._owner_list, self.hp, self.res, ctl_dev=ctl)
+        else:
+            for a, b in self.owners:
+                args = (self.master[a:b], self.exp_avg[a:b], self.exp_avg_sq[a:b],
+                        self.param16[a:b], red[a:b], self.hp)
+                if ctl is None:
+                    zero_adamw_step(*args, self.res)
+                else:
+                    zero_adamw_step_ctl(*args, ctl, self.res)
         if ctl is not None:
             zero_step_control_update(ctl, self.res)
         if marks:
