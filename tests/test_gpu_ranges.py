@@ -1,7 +1,7 @@
 """The range-list calls on the GPU against the oracle, every element:
 zero_reduce_check_ranges and zero_adamw_step_ranges over disjoint ranges of
-random sizes and alignments (empty ranges, ranges one element apart, more
-than 32 ranges so that several launches share one fold of the norm), with
+random sizes and alignments (empty ranges, ranges one element apart, lists
+of up to a few dozen ranges, one launch each, sharing one fold of the norm), with
 the result and inv_scale given on the host or read from a device step
 control; elements outside the ranges untouched.
 
