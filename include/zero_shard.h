@@ -359,11 +359,11 @@ int zero_step_control_update(zero_step_control* ctl, const zero_step_result* res
  * the single-range call on each range in list order (zero_reduce_check_owned
  * with accumulate != 0 after the first, zero_adamw_step per range), except
  * that sumsq adds the per-block partials of all ranges in one fold, so its
- * last bits may differ from the chained calls'.  Each range is one launch of
+ * last bits may differ from the chained calls'.  Ranges that touch (one ends
+ * where another begins) are merged, and each merged range is one launch of
  * the single-range kernel; the reduce writes every range's block partials
  * into one workspace and folds the norm once (the chained calls launch a
- * fold and a finalize per range), so a list of many small ranges costs one
- * launch per range plus one fold.
+ * fold and a finalize per range).
  *   ranges[n_ranges]  host array, read during the call; offsets and counts
  *                     >= 0; no element may lie in two ranges (ZERO_EINVAL;
  *                     ZERO_ERANGE when offset + count overflows int64);

@@ -1,7 +1,8 @@
 """The range-list calls on the GPU against the oracle, every element:
 zero_reduce_check_ranges and zero_adamw_step_ranges over disjoint ranges of
-random sizes and alignments (empty ranges, ranges one element apart, lists
-of up to a few dozen ranges, one launch each, sharing one fold of the norm), with
+random sizes and alignments (empty ranges, ranges one element apart, ranges
+that touch and are merged into one launch, touching ranges that tile the whole
+buffer, lists of up to 70 ranges sharing one fold of the norm), with
 the result and inv_scale given on the host or read from a device step
 control; elements outside the ranges untouched.
 
@@ -46,15 +47,29 @@ def _dev32(a, offset=0):
 
 
 def _random_ranges(total, k, rng):
-    """k disjoint ranges in [0, total) in random order: random gaps (some 0
-    or 1 element), random lengths, a few empty ranges."""
+    """k disjoint ranges in [0, total) in random order: random gaps (about a
+    third of the ranges touch the one before, which the library merges into
+    one launch), random lengths, a few empty ranges."""
     cuts = np.sort(rng.choice(np.arange(1, total), size=2 * k, replace=False))
     rs = []
     for j in range(k):
         a, b = int(cuts[2 * j]), int(cuts[2 * j + 1])
+        if j > 0 and rng.random() < 0.3:
+            a = int(cuts[2 * j - 1])               # starts where the previous ends
         if rng.random() < 0.1:
             b = a                                  # empty
         rs.append((a, b - a))
+    order = rng.permutation(len(rs))
+    return [rs[i] for i in order]
+
+
+def _tiling_ranges(total, k, rng):
+    """k ranges that cover [0, total) exactly, each touching the next, in
+    random order (a few empty)."""
+    cuts = np.concatenate([[0], np.sort(rng.choice(np.arange(1, total), size=k - 1,
+                                                   replace=False)), [total]])
+    rs = [(int(cuts[j]), int(cuts[j + 1] - cuts[j])) for j in range(k)]
+    rs += [(int(rng.integers(0, total)), 0) for _ in range(2)]
     order = rng.permutation(len(rs))
     return [rs[i] for i in order]
 
@@ -100,6 +115,48 @@ def test_reduce_check_ranges_parity(dtype, n_ranks, k, offset, in_place, control
     assert r.overflow == flag and r.inv_scale == np.float32(inv)
     if not flag:
         assert r.sumsq == pytest.approx(sumsq, rel=1e-12, abs=0)
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("n_ranks", [8, 16])
+@pytest.mark.parametrize("k", [2, 18])
+@pytest.mark.parametrize("offset", [0, 5])
+def test_ranges_tiling_whole_buffer(dtype, n_ranks, k, offset):
+    """Touching ranges that cover the whole buffer (a bucket group's windows
+    with every owner on one GPU): merged into one launch per call; reduce,
+    flag, norm and AdamW equal the oracle over the whole buffer."""
+    total = 900_017
+    rng = np.random.default_rng(1000 + 10 * dtype + n_ranks + k + offset)
+    host = [_rand16(total, dtype, rng) for _ in range(n_ranks)]
+    srcs = [_dev16(h, dtype, offset) for h in host]
+    dst = _dev16(np.zeros(total, np.uint16), dtype, offset)
+    ranges = _tiling_ranges(total, k, rng)
+    inv = 2.0 ** -10 if dtype == FP16 else 1.0
+    res = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ws = torch.empty(Z.zero_range_workspace_bytes(ranges) // 8 + 1, dtype=torch.float64,
+                     device="cuda")
+    Z.zero_reduce_check_ranges(dst, srcs, ranges, inv, res, ws)
+    want_red = oracle.reduce(host, dtype)
+    assert_bits16_equal(to_np16(dst), want_red, dtype, "reduce over the tiling")
+    flag, sumsq = oracle.check(want_red, dtype, inv)
+    r = Z.read_result(res)
+    assert r.overflow == flag == 0
+    assert r.sumsq == pytest.approx(sumsq, rel=1e-12, abs=0)
+    master = (rng.standard_normal(total) * 0.02).astype(np.float32)
+    p16 = oracle.encode16(master, dtype)
+    d = [_dev32(x, offset) for x in (master, np.zeros(total, np.float32),
+                                     np.zeros(total, np.float32))]
+    d_p16 = _dev16(p16, dtype, offset)
+    hp = oracle.HParams(max_grad_norm=1.0)
+    Z.zero_adamw_step_ranges(*d, d_p16, dst, ranges,
+                             Z.zero_adamw_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps,
+                                                  hp.weight_decay, hp.max_grad_norm, 1), res)
+    torch.cuda.synchronize()
+    want = [master.copy(), np.zeros(total, np.float32), np.zeros(total, np.float32), p16.copy()]
+    oracle.adamw(*want, want_red, dtype, inv, sumsq, flag, hp, 1)
+    for dev, w, kk in zip(d, want, ("master", "exp_avg", "exp_avg_sq")):
+        assert_f32_close(to_np32(dev), w, kk)
+    assert_p16_close(to_np16(d_p16), want[3], dtype, "param16")
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])
