@@ -1,7 +1,8 @@
 """bench.py end to end on the GPU, on the small shards: one JSON line with
 the fields of its contract, whole steps counted, the roofline entry present,
 and the measured placement reported (device-resident and host step control,
-and the inf/NaN protocol of the fragmented-bucket workload)."""
+and the inf/NaN protocol of the fragmented-bucket workload); and the smoke()
+entry point."""
 import json
 import os
 import subprocess
@@ -47,3 +48,10 @@ def test_buckets_overflow_protocol():
     assert b["applied_steps"] == 12 and b["skipped_steps"] == 4
     assert b["final_loss_scale"] == 2.0 ** 12
     assert b["final_norm"] is None              # the last step overflowed
+
+
+def test_smoke_entry_point():
+    """The round-end entry point: one small owner step on cuda:0, checked
+    against the oracle inside smoke() itself (it raises on a mismatch)."""
+    import __graft_entry__
+    __graft_entry__.smoke()
