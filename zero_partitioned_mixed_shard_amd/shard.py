@@ -15,7 +15,8 @@ runs one step as the library's calls:
 With several reduce windows or owners (a bucketed group with all owners on
 one GPU, round-robin ownership with one window per owned tensor) the fused
 step makes one range-list call for all windows (zero_reduce_check_ranges)
-and one for all owners (zero_adamw_step_ranges); batched=False keeps one
+and one for all owners (zero_adamw_step_ranges); the library merges ranges
+that touch into one launch and folds the norm once.  batched=False keeps one
 call per window and per owner.
 
 With fused=False the reduce and the check are separate calls
