@@ -185,15 +185,17 @@ def test_check_parity(dtype, count, offset, specials):
         assert r.sumsq == pytest.approx(sumsq, rel=1e-12, abs=0)
 
 
+# the large size only at the workload rank counts
+FUSED_CASES = ([(n, c) for n in (1, 3, 8, 16) for c in REDUCE_COUNTS]
+               + [(n, 10_000_019) for n in (8, 16)])
+
+
 @pytest.mark.parametrize("dtype", [FP16, BF16])
-@pytest.mark.parametrize("n_ranks", [1, 3, 8, 16])
-@pytest.mark.parametrize("count", REDUCE_COUNTS + [10_000_019])
+@pytest.mark.parametrize("n_ranks,count", FUSED_CASES)
 @pytest.mark.parametrize("offset", [0, 3])
 def test_reduce_check_fused_parity(dtype, n_ranks, count, offset):
     """zero_reduce_check_owned = reduce then check; 10,000,019 elements give
     2,442 block partials, folded by the one-block final pass."""
-    if count > 1_000_000 and n_ranks not in (8, 16):
-        pytest.skip("large size only at the workload rank counts")
     rng = np.random.default_rng(7 * dtype + 31 * n_ranks + count % 101 + offset)
     host = [_rand16(count, dtype, rng, specials=0.0 if count > 1000 else 0.01)
             for _ in range(n_ranks)]
