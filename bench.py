@@ -13,9 +13,11 @@ Algorithmic HBM bytes per owned element: 2N + 2 for reduce+check (2N + 4 with
 Default workload: owner 0's partition of the LLaMA-70B-shaped flat buffer
 (68,976,648,192 parameters, N = 8 ranks, 8,622,081,024 owned elements, bf16
 gradients N(0, 1e-4), AdamW lr 1e-3, betas (0.9, 0.999), eps 1e-8, wd 0.01,
-clip 1.0), the largest configuration that fits one GPU: 258.7 GB resident,
-the reduce writing in place into rank 0's buffer.  --workload llama7b runs the
-LLaMA-7B-shaped shard (842,301,952 owned elements, separate reduced buffer).
+clip 1.0), the largest configuration that fits one GPU: 275.9 GB resident
+with the reduced gradient in a buffer of its own (258.7 GB with
+--in-place-reduce, the reduce then writing into rank 0's buffer).
+--workload llama7b runs the LLaMA-7B-shaped shard (842,301,952 owned
+elements).
 
 Prints one JSON line: params updated per second (owned elements x applied
 steps / time), per-phase times measured with HIP events on the stream the
@@ -105,6 +107,10 @@ def parse():
                          "occurrences) or NaN (even) at a seeded index: the step is skipped "
                          "and the loss scale halves; 0 = off (default 4 for the buckets "
                          "workload, whose protocol has an overflow every 4th step; else 0)")
+    ap.add_argument("--in-place-reduce", action="store_true",
+                    help="LLaMA-70B / 7B shard: reduce into rank 0's buffer instead of a reduced "
+                         "buffer of its own (17.2 GB less at the 70B size; the separate buffer "
+                         "measured 0.5-1 %% faster there)")
     ap.add_argument("--no-batch", action="store_true",
                     help="one reduce+check call per reduce window and one AdamW call per owner, "
                          "instead of one range-list call each (bucket group, round-robin owner)")
@@ -189,10 +195,10 @@ def cpu_baseline(wl, begin: int, seconds: float) -> dict:
 
 def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                 device_control: bool = False, placement: str = "auto", arena_slack: int = 0,
-                batched: bool = True):
+                batched: bool = True, in_place: bool = False):
     """Owner 0's shard of `wl` as the bench runs it: state, reduced gradient
-    and the N rank buffers (the LLaMA-70B shard reduces in place into rank 0's
-    buffer), initial 16-bit weights and one gradient batch generated on the
+    (a buffer of its own, or with in_place rank 0's buffer) and the N rank
+    buffers, initial 16-bit weights and one gradient batch generated on the
     device.  Returns (shard, begin, end, padded, in_place)."""
     import torch
 
@@ -202,7 +208,6 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
 
     offs, parts, padded = Z.zero_partition_layout(wl.numels, wl.world, wl.align)
     begin, end = int(parts[0]), int(parts[1])
-    in_place = wl.name == "llama70b"       # 8 rank buffers + state fill ~259 GB
     shard = ShardStep(begin, end, [(begin, end)], wl.dtype, lr=wl.lr, beta1=wl.beta1,
                       beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
@@ -392,7 +397,7 @@ def main():
         shard, begin, end, padded, in_place = build_shard(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
             fused=not args.unfused, device_control=not args.host_control, placement=args.placement,
-            arena_slack=slack, batched=not args.no_batch)
+            arena_slack=slack, batched=not args.no_batch, in_place=args.in_place_reduce)
     count = end - begin
     bufs = shard.rank_bufs
 

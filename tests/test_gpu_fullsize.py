@@ -2,7 +2,8 @@
 
 * LLaMA-7B-shaped owner-0 shard (842,301,952 elements, N = 8 bf16 ranks, clip
   1.0, 5 steps) and LLaMA-70B-shaped owner-0 shard (8,622,081,024 elements,
-  in-place reduce into rank 0's buffer, 3 steps), with the same resident
+  3 steps; a separate reduced buffer, and with host control the in-place
+  reduce into rank 0's buffer), with the same resident
   gradient batch every step as in the bench.  The oracle recomputes the
   overflow flag and the squared norm of the whole shard on the host
   (regenerating all N ranks' gradients chunk by chunk), and follows sampled
@@ -134,12 +135,14 @@ class SampledOracle:
 @pytest.mark.parametrize("name", ["llama7b", "llama70b"])
 def test_llama_shard_fullsize_sampled(name, device_control):
     """device_control=True is the bench's default launch configuration (the
-    *_ctl calls and the control update); False the host loss scaler."""
+    *_ctl calls and the control update, the reduced gradient in a buffer of
+    its own); False the host loss scaler, and at the 70B size the
+    memory-minimal reduce into rank 0's buffer (bench.py --in-place-reduce)."""
     wl = W.WORKLOADS[name]
     offs, parts, padded = oracle.layout(wl.numels, wl.world, wl.align)
     begin, end = int(parts[0]), int(parts[1])
     count = end - begin
-    in_place = name == "llama70b"
+    in_place = name == "llama70b" and not device_control
     need = count * (12 + 2 + (0 if in_place else 2) + 2 * wl.world) + (1 << 30)
     free = _free_device_memory()
     if free < need:
@@ -147,7 +150,7 @@ def test_llama_shard_fullsize_sampled(name, device_control):
     t0 = time.time()
     print(f"{name}: {count} owned elements, {wl.world} ranks, in_place={in_place}", flush=True)
     # as bench.py runs it (measured placement; its arena slack moves buffers only)
-    shard, _, _, _, _ = bench.build_shard(wl, device_control=device_control)
+    shard, _, _, _, _ = bench.build_shard(wl, device_control=device_control, in_place=in_place)
     bufs = shard.rank_bufs
     flag_o, sumsq_o = host_full_check(wl, begin, end, padded, 1, wl.scale0)
     print(f"{name}: oracle full-shard norm {math.sqrt(sumsq_o):.9g} ({time.time() - t0:.1f} s)",
