@@ -35,8 +35,12 @@ def test_toy_json_line(control):
     assert "model" not in b["config"] and "workload" in b["config"]
     r = b["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and 0 < r["frac"] < 1
-    assert r["achieved"] == pytest.approx(28 * b["config"]["owned_elems"]
-                                          / (b["phases"]["adamw"]["ms"] * 1e-3) / 1e9, rel=1e-3)
+    # the dominant kernel of the step: the longer of the two phases
+    dom = max(("adamw", "reduce_check"), key=lambda k: b["phases"][k]["ms"])
+    assert r["kernel"].startswith({"adamw": "adamw_kernel", "reduce_check": "reduce_kernel"}[dom])
+    assert r["achieved"] == pytest.approx(b["phases"][dom]["bytes_per_elem"]
+                                          * b["config"]["owned_elems"]
+                                          / (b["phases"][dom]["ms"] * 1e-3) / 1e9, rel=1e-3)
     assert b["config"]["placement_setup_ms"] and "buffer order" in b["config"]["placement"]
     assert b["final_norm"] is not None and b["final_norm"] > 0
 
@@ -48,6 +52,10 @@ def test_buckets_overflow_protocol():
     assert b["applied_steps"] == 12 and b["skipped_steps"] == 4
     assert b["final_loss_scale"] == 2.0 ** 12
     assert b["final_norm"] is None              # the last step overflowed
+    # 16 ranks: the reduce (34 B per element) outweighs AdamW (28 B)
+    r = b["roofline"]
+    assert r["kernel"].startswith("reduce_kernel") and 0 < r["frac"] < 1
+    assert b["phases"]["reduce_check"]["ms"] > b["phases"]["adamw"]["ms"]
 
 
 def test_smoke_entry_point():
