@@ -197,9 +197,10 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
                 device_control: bool = False, placement: str = "auto", arena_slack: int = 0,
                 batched: bool = True, in_place: bool = False):
     """Owner 0's shard of `wl` as the bench runs it: state, reduced gradient
-    (a buffer of its own, or with in_place rank 0's buffer) and the N rank
-    buffers, initial 16-bit weights and one gradient batch generated on the
-    device.  Returns (shard, begin, end, padded, in_place)."""
+    (a buffer of its own, or with in_place -- or when the device cannot hold
+    a separate one -- rank 0's buffer) and the N rank buffers, initial 16-bit
+    weights and one gradient batch generated on the device.  Returns (shard,
+    begin, end, padded, in_place)."""
     import torch
 
     from synth import inputs as I
@@ -208,6 +209,12 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
 
     offs, parts, padded = Z.zero_partition_layout(wl.numels, wl.world, wl.align)
     begin, end = int(parts[0]), int(parts[1])
+    if not in_place:
+        # a reduced buffer of its own needs 2 B per element more; where the
+        # device cannot hold it (with 4 GiB to spare), reduce into rank 0's
+        # buffer instead (reported as config.in_place_reduce)
+        need = (end - begin) * (12 + 2 + 2 + 2 * wl.world) + (4 << 30)
+        in_place = torch.cuda.mem_get_info()[0] < need
     shard = ShardStep(begin, end, [(begin, end)], wl.dtype, lr=wl.lr, beta1=wl.beta1,
                       beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,

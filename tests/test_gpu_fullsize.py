@@ -150,7 +150,9 @@ def test_llama_shard_fullsize_sampled(name, device_control):
     t0 = time.time()
     print(f"{name}: {count} owned elements, {wl.world} ranks, in_place={in_place}", flush=True)
     # as bench.py runs it (measured placement; its arena slack moves buffers only)
-    shard, _, _, _, _ = bench.build_shard(wl, device_control=device_control, in_place=in_place)
+    # the layout bench.py settles on (in place where a separate buffer does not fit)
+    shard, _, _, _, in_place = bench.build_shard(wl, device_control=device_control,
+                                                 in_place=in_place)
     bufs = shard.rank_bufs
     flag_o, sumsq_o = host_full_check(wl, begin, end, padded, 1, wl.scale0)
     print(f"{name}: oracle full-shard norm {math.sqrt(sumsq_o):.9g} ({time.time() - t0:.1f} s)",
