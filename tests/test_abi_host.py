@@ -231,3 +231,29 @@ def test_range_lists_are_checked_before_launching():
         Z.zero_check_workspace_bytes(10_000_019)
     assert Z.zero_range_workspace_bytes([(0, 4096), (4096, 4096)]) >= \
         Z.zero_check_workspace_bytes(8192)
+
+
+def test_header_compiles_as_c(tmp_path):
+    """include/zero_shard.h is a C header: a C11 translation unit that uses
+    its types and a declaration compiles, with no diagnostic from the header
+    itself (HIP's runtime API header supplies hipStream_t)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "zero_shard.h"\n'
+                   "int main(void) {\n"
+                   "    zero_range r = {0, 1};\n"
+                   "    zero_tensor_desc d = {0, 0, 0, 0};\n"
+                   "    zero_step_result s;\n"
+                   "    (void)d; (void)s;\n"
+                   "    return (int)zero_range_workspace_bytes(&r, 1) * 0;\n"
+                   "}\n")
+    r = subprocess.run([gcc, "-x", "c", "-std=c11", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.dirname(HEADER), "-I", "/opt/rocm/include", "-fsyntax-only",
+                        str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    own = [l for l in r.stderr.splitlines() if "zero_shard.h:" in l and "included from" not in l]
+    assert not own, own
