@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SRCS = [os.path.join(ROOT, "zero_partitioned_mixed_shard_amd", "csrc", f)
                for f in ("zero_common.h", "zero_shard.hip")]
 COUNTERS = {w: os.path.join(ROOT, "profiles", f"adamw_reduce_{w}_hbm_counters.md")
-            for w in ("llama7b", "llama70b")}
+            for w in ("toy", "bert", "llama7b", "llama70b")}
 
 
 def measured_traffic(kernel: str, workload: str):
