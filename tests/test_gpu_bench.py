@@ -63,3 +63,14 @@ def test_smoke_entry_point():
     against the oracle inside smoke() itself (it raises on a mismatch)."""
     import __graft_entry__
     __graft_entry__.smoke()
+
+
+def test_in_place_reduce_option():
+    """--in-place-reduce: the sum goes into rank 0's buffer, reported in the
+    config; the line is otherwise complete."""
+    b = _bench("--workload", "toy", "--steps", "3", "--warmup", "1", "--in-place-reduce")
+    assert b["config"]["in_place_reduce"] is True
+    assert b["applied_steps"] == 3 and b["value"] > 0
+    assert b["roofline"]["traffic"] is None or b["roofline"]["traffic"] > 0
+    d = _bench("--workload", "toy", "--steps", "3", "--warmup", "1")
+    assert d["config"]["in_place_reduce"] is False
