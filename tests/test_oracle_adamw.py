@@ -133,7 +133,10 @@ def test_matches_torch_adamw_step_by_step(max_norm):
     # clipping adds torch's fp32 norm and coefficient (a few ulp) to both sides' terms
     tol = 4 * EPS32 if max_norm >= 1.0 else 12 * EPS32
     assert worst["m"] <= tol
-    assert worst["v"] <= 2 * tol
+    # unclipped, v = b2*v + (1-b2)*g^2 rounds three times on each side: 4 ulp
+    # of its magnitude bound the difference.  Clipped, both g^2 terms carry
+    # twice the relative difference of the two fp32 clip factors.
+    assert worst["v"] <= (tol if max_norm >= 1.0 else 2 * tol)
     assert worst["p"] <= 2.0
 
 
