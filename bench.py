@@ -15,9 +15,14 @@ Default workload: owner 0's partition of the LLaMA-70B-shaped flat buffer
 gradients N(0, 1e-4), AdamW lr 1e-3, betas (0.9, 0.999), eps 1e-8, wd 0.01,
 clip 1.0), the largest configuration that fits one GPU: 275.9 GB resident
 with the reduced gradient in a buffer of its own (258.7 GB with
---in-place-reduce, the reduce then writing into rank 0's buffer).
---workload llama7b runs the LLaMA-7B-shaped shard (842,301,952 owned
-elements).
+--in-place-reduce, the reduce then writing into rank 0's buffer).  The
+ranks' gradients arrive bucket by bucket (5e8-element, tensor-aligned reduce
+buckets; each bucket's 8 slices back to back), and the buffers sit in one
+arena in a fixed order (ranks_first, master / m / v at least 32 GiB apart):
+no placement search unless --placement auto.  After the 70B shard is freed
+the LLaMA-7B-shaped shard (842,301,952 owned elements) is timed the same way
+and reported as the "secondary" object (--secondary none skips it;
+--workload llama7b runs it alone).
 
 Prints one JSON line: params updated per second (owned elements x applied
 steps / time), per-phase times measured with HIP events on the stream the
@@ -86,18 +91,29 @@ def parse():
                          "i mod N == this owner (packed; one reduce window per tensor)")
     ap.add_argument("--no-arena", action="store_true",
                     help="separate allocations instead of one arena with spread placement")
-    ap.add_argument("--placement", default="auto",
-                    choices=["auto", "interleaved", "rank_block", "rank_block_b", "master_ranks",
-                             "streams_first", "ranks_first"],
-                    help="order of the buffers in the arena; auto times every order once at "
-                         "setup (outside the timed steps) and keeps the fastest")
-    ap.add_argument("--arena-slack-gib", type=float, default=64.0,
+    ap.add_argument("--placement", default="ranks_first",
+                    choices=["auto", "spread", "interleaved", "rank_block", "rank_block_b",
+                             "master_ranks", "streams_first", "ranks_first"],
+                    help="order of the buffers in the arena (default ranks_first: the rank "
+                         "data, then master, m, v, the 16-bit copy and the reduced gradient, "
+                         "with --min-gap-gib between master, m and v); auto times every order "
+                         "at setup (outside the timed steps) and keeps the fastest")
+    ap.add_argument("--secondary", default=None,
+                    help="a second workload timed in the same run after the first is freed, "
+                         "reported as the 'secondary' object (default: llama7b after llama70b; "
+                         "'none' to skip)")
+    ap.add_argument("--secondary-steps", type=int, default=20)
+    ap.add_argument("--arena-slack-gib", type=float, default=0.0,
                     help="allocate the arena up to this much larger (never more than is free, "
                          "less 4 GiB) and let --placement auto also try every order at base "
                          "offsets 4 GiB apart inside it, i.e. at other physical addresses; 0 = "
                          "an arena of exactly the working set")
-    ap.add_argument("--min-gap-gib", type=float, default=0.0,
-                    help="minimum distance between the AdamW streams' bases in the arena")
+    ap.add_argument("--min-gap-gib", type=float, default=32.0,
+                    help="minimum distance between the bases of master, m and v in the arena "
+                         "(halved, down to 0, where the device cannot hold it)")
+    ap.add_argument("--bucket-cap", type=float, default=None,
+                    help="reduce bucket size in elements for the LLaMA shards (default 5e8, "
+                         "the pages' reduce_bucket_size)")
     ap.add_argument("--flush-gib", type=float, default=0.0,
                     help="write this much scratch memory between timed steps (untimed), so that "
                          "no step finds its inputs in the 256 MB Infinity Cache or the L2; "
@@ -125,7 +141,13 @@ def parse():
     ap.add_argument("--write-back", action="store_true",
                     help="buckets workload: also scatter the updated 16-bit flat buffer into "
                          "per-parameter tensors after AdamW (zero_flat_scatter), timed as a phase")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.secondary is None:
+        args.secondary = ("llama7b" if args.workload == "llama70b" and args.round_robin_owner is None
+                          else "none")
+    if args.secondary == "none":
+        args.secondary = None
+    return args
 
 
 def cpu_baseline(wl, begin: int, seconds: float) -> dict:
@@ -193,17 +215,24 @@ def cpu_baseline(wl, begin: int, seconds: float) -> dict:
             "phase_params_per_s": {k: round(n * steps / v, 1) for k, v in phase.items()}}
 
 
-def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
-                device_control: bool = False, placement: str = "auto", arena_slack: int = 0,
-                batched: bool = True, in_place: bool = False):
+def build_shard(wl, arena: bool = True, min_gap: int = 32 << 30, fused: bool = True,
+                device_control: bool = False, placement: str = "ranks_first",
+                arena_slack: int = 0, batched: bool = True, in_place: bool = False,
+                bucket_cap=None):
     """Owner 0's shard of `wl` as the bench runs it: state, reduced gradient
     (a buffer of its own, or with in_place -- or when the device cannot hold
-    a separate one -- rank 0's buffer) and the N rank buffers, initial 16-bit
-    weights and one gradient batch generated on the device.  Returns (shard,
-    begin, end, padded, in_place)."""
+    a separate one -- rank 0's buffer), the N ranks' gradients, initial
+    16-bit weights and one gradient batch generated on the device.  With a
+    reduced buffer of its own and the fused reduce+check, the ranks'
+    gradients arrive bucket by bucket (ZeRO-2 source walkthrough section
+    4.2: reduce buckets of reduce_bucket_size = 5e8 elements, tensor-aligned):
+    each bucket's N slices of the owner's partition lie back to back, and one
+    zero_reduce_check_buckets call reduces every bucket.  Otherwise each rank
+    has one flat buffer.  Returns (shard, begin, end, padded, in_place)."""
     import torch
 
     from synth import inputs as I
+    from synth import workloads as W
     import zero_partitioned_mixed_shard_amd as Z
     from zero_partitioned_mixed_shard_amd.shard import ShardStep
 
@@ -215,16 +244,21 @@ def build_shard(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
         # buffer instead (reported as config.in_place_reduce)
         need = (end - begin) * (12 + 2 + 2 + 2 * wl.world) + (4 << 30)
         in_place = torch.cuda.mem_get_info()[0] < need
+    cap = int(bucket_cap or wl.bucket_cap or 0)
+    layout = "bucket" if fused and not in_place and cap else "flat"
+    windows = None
+    if layout == "bucket":
+        windows = W.bucket_windows(wl, offs, padded, Z.zero_bucket_layout(wl.numels, cap))
     shard = ShardStep(begin, end, [(begin, end)], wl.dtype, lr=wl.lr, beta1=wl.beta1,
                       beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
                       max_grad_norm=wl.clip, scale0=wl.scale0, min_scale=wl.min_scale,
-                      window=wl.window, in_place_rank=0 if in_place else None, fused=fused,
-                      own_ranks=True, world=wl.world, arena=arena, min_gap=min_gap,
+                      window=wl.window, windows=windows, in_place_rank=0 if in_place else None,
+                      fused=fused, own_ranks=True, world=wl.world, arena=arena, min_gap=min_gap,
                       device_control=device_control, placement=placement,
-                      arena_slack=arena_slack, batched=batched)
+                      arena_slack=arena_slack, batched=batched, rank_layout=layout)
     shard.load_param16(I.device_param16(wl, offs, begin, end, out=shard.param16))
-    for r, buf in enumerate(shard.rank_bufs):
-        I.device_rank_grad(wl, 1, wl.scale0, r, begin, end, padded, out=buf)
+    shard.fill_ranks(lambda r, a, b, out: I.device_rank_grad(wl, 1, wl.scale0, r, begin + a,
+                                                             begin + b, padded, out=out))
     torch.cuda.synchronize()
     return shard, begin, end, padded, in_place
 
@@ -334,38 +368,20 @@ def build_round_robin(wl, owner: int, arena: bool = True, min_gap: int = 0, fuse
     return shard, count, len(owned), max(per_owner) / (sum(per_owner) / wl.world)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "runs on one GPU only: the owner-shard step is "
-                          "measured on one GPU's partition; run with --gpus 1"}), file=sys.stderr)
-        sys.exit(2)
-    if args.steps is None:
-        args.steps = 40 if args.workload == "buckets" else 20
-    if args.inject_every is None:
-        args.inject_every = 4 if args.workload == "buckets" else 0
-    if args.inject_every < 0 or args.inject_every == 1:
-        print(json.dumps({"error": "--inject-every takes 0 (off) or K >= 2, so that some "
-                          "steps run whole"}), file=sys.stderr)
-        sys.exit(2)
-    if args.graph and args.host_control:
-        print(json.dumps({"error": "--graph replays a step with device-resident control; it "
-                          "cannot be combined with --host-control"}), file=sys.stderr)
-        sys.exit(2)
-    if args.write_back and args.workload != "buckets":
-        print(json.dumps({"error": "--write-back applies to --workload buckets"}), file=sys.stderr)
-        sys.exit(2)
+def run_workload(args, workload: str, steps: int, inject_every: int,
+                 calibrate: bool = False) -> dict:
+    """Builds `workload` as the bench runs it, does the warm-up steps, times
+    `steps` steps and returns the measured fields (and the owned range under
+    "_begin"), then frees the device memory it used."""
     import numpy as np
     import torch
 
-    from synth import inputs as I
     from synth import workloads as W
     import zero_partitioned_mixed_shard_amd as Z
-    from zero_partitioned_mixed_shard_amd.shard import ShardStep
 
-    wl = W.WORKLOADS[args.workload]
+    wl = W.WORKLOADS[workload]
     torch.cuda.set_device(0)
-    if args.copy_calibration_gib > 0:
+    if calibrate and args.copy_calibration_gib > 0:
         # one elementwise kernel that reads and writes exactly `nbytes` each:
         # the reference for scaling the HBM byte counters
         nbytes = int(args.copy_calibration_gib * 2 ** 30)
@@ -384,7 +400,7 @@ def main():
     if args.flush_gib > 0:
         # allocated before the shard: the arena's slack is clamped to what is left
         flush = torch.empty(int(args.flush_gib * 2 ** 30) // 4, dtype=torch.float32, device="cuda")
-    if args.round_robin_owner is not None:
+    if args.round_robin_owner is not None and workload == args.workload:
         shard, count_rr, n_owned, imbalance = build_round_robin(
             wl, args.round_robin_owner, arena=not args.no_arena,
             min_gap=int(args.min_gap_gib * 2 ** 30), fused=not args.unfused,
@@ -393,7 +409,7 @@ def main():
         begin, end, padded, in_place = 0, count_rr, 0, False
         rr_info = {"owner": args.round_robin_owner, "owned_tensors": n_owned,
                    "owned_elems": count_rr, "largest_over_mean_owner": round(imbalance, 4)}
-    elif args.workload == "buckets":
+    elif workload == "buckets":
         shard, copy_in, padded, write_back = build_buckets(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
             fused=not args.unfused, write_back=args.write_back,
@@ -404,10 +420,10 @@ def main():
         shard, begin, end, padded, in_place = build_shard(
             wl, arena=not args.no_arena, min_gap=int(args.min_gap_gib * 2 ** 30),
             fused=not args.unfused, device_control=not args.host_control, placement=args.placement,
-            arena_slack=slack, batched=not args.no_batch, in_place=args.in_place_reduce)
+            arena_slack=slack, batched=not args.no_batch, in_place=args.in_place_reduce,
+            bucket_cap=args.bucket_cap)
     count = end - begin
-    bufs = shard.rank_bufs
-
+    bufs = shard.rank_bufs if shard.rank_layout == "flat" else None
 
     def one_step(marks=None):
         """Enqueue one step.  With device-resident control nothing is read
@@ -429,7 +445,7 @@ def main():
         one_step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     applied = 0
     infos = []
     last_sumsq = None
@@ -450,19 +466,20 @@ def main():
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
     injections = 0
-    for k in range(args.steps):
+    for k in range(steps):
         Z.zero_partition_layout(wl.numels, wl.world, wl.align)
         if flush is not None:
             flush.fill_(float(k))                  # evicts the caches; outside the step's events
         planted = None
-        if args.inject_every and (k + 1) % args.inject_every == 0:
-            # a rank whose buffer the copy-in does not rewrite; seeded index
+        if inject_every and (k + 1) % inject_every == 0:
+            # a rank whose data the copy-in does not rewrite; seeded index
             injections += 1
-            r = 1 + (k % (len(bufs) - 1)) if len(bufs) > 1 else 0
+            r = 1 + (k % (shard.n_ranks - 1)) if shard.n_ranks > 1 else 0
             idx = (k * 2654435761 + 12345) % count
             bad = float("inf") if injections % 2 else float("nan")
-            planted = (bufs[r], idx, bufs[r][idx:idx + 1].clone())
-            bufs[r][idx:idx + 1].fill_(bad)
+            cell = shard.rank_element(r, idx)
+            planted = (cell, cell.clone())
+            cell.fill_(bad)
         if graph is not None:
             ev[k][0].record()
             graph.replay()
@@ -476,8 +493,8 @@ def main():
                 applied += info.applied
                 infos.append(info)
         if planted is not None:
-            buf, idx, old = planted
-            buf[idx:idx + 1].copy_(old)
+            cell, old = planted
+            cell.copy_(old)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -512,8 +529,7 @@ def main():
         bytes_per["write_back"] = 4
     # steps that ran whole: an injected overflow makes AdamW return early, so
     # phase rates, the roofline and step_GBps average over the other steps only
-    whole = [k for k in range(args.steps)
-             if not (args.inject_every and (k + 1) % args.inject_every == 0)]
+    whole = [k for k in range(steps) if not (inject_every and (k + 1) % inject_every == 0)]
     phases = {}
     for k, v in ms.items():
         avg = float(np.mean([v[i] for i in whole]))
@@ -526,8 +542,8 @@ def main():
     per_step = [e[first].elapsed_time(e[last]) for e in ev]
     if flush is not None:                          # the flushes sit between the steps' events
         total_ms = float(sum(per_step))
-    step_ms = total_ms / args.steps
-    whole_ms = step_ms if not args.inject_every else float(np.mean([per_step[i] for i in whole]))
+    step_ms = total_ms / steps
+    whole_ms = step_ms if not inject_every else float(np.mean([per_step[i] for i in whole]))
     step_bytes = sum(bytes_per.values()) * count
     # the roofline entry is for the step's dominant kernel: AdamW on the LLaMA
     # shards (28 of 46 B per element), the fused reduce+check on the 16-rank
@@ -547,7 +563,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(kernels[dom][0], args.workload),
+            "traffic": measured_traffic(kernels[dom][0], workload),
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, "
                             "factors from a known-size elementwise kernel)",
         }
@@ -557,44 +573,42 @@ def main():
     shard_scale = shard.scale
     last = infos[-1].sumsq if infos else last_sumsq
     final_norm = float(np.sqrt(last)) if last is not None and np.isfinite(last) else None
-    result = {
-        "metric": "params updated/s per GPU (ZeRO shard AdamW step) + achieved HBM GB/s % of peak",
+    layout = ("separate allocations" if args.no_arena else
+              f"one arena, buffer order {shard.placement}"
+              + (" (fastest of the orders timed at setup)" if args.placement == "auto" else "")
+              + (f", master / m / v at least {shard.fp32_gap / 2 ** 30:g} GiB apart"
+                 if shard.fp32_gap else ""))
+    rank_data = ("each reduce bucket's N rank slices back to back" if shard.rank_layout == "bucket"
+                 else "one flat buffer per rank")
+    reduced = "in place, in rank 0's buffer" if in_place else "a buffer of its own"
+    out = {
         "value": count * applied / (total_ms * 1e-3),
-        "unit": "params/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp32",
-        "data": "synthetic",
         "config": {
-            "workload": (f"{wl.name}-shaped owner-0 shard" if args.workload != "buckets" else
+            "workload": (f"{wl.name}-shaped owner-0 shard" if workload != "buckets" else
                          "10,000-tensor group, all owners, copy-in + bucketed reduce + AdamW"
                          + (" + write-back" if write_back else ""))
                         if rr_info is None else
                         f"{wl.name}-shaped, round-robin owner {rr_info['owner']} (whole tensors)",
             "round_robin": rr_info,
-            "description": wl.description,
+            "description": f"{wl.description}; rank data: {rank_data}; reduced gradient: "
+                           f"{reduced}",
             "owned_elems": count,
             "ranks": wl.world,
             "grad_dtype": "bf16" if wl.dtype == Z.ZERO_BF16 else "fp16",
             "clip": wl.clip,
             "in_place_reduce": in_place,
+            "rank_layout": shard.rank_layout,
+            "reduce_windows": len(shard.reduce_ranges),
             "fused_reduce_check": not args.unfused,
             "range_list_calls": not args.no_batch,
             "step_control": "host (16-byte readback per step)" if args.host_control else
                             "device-resident (no per-step readback)",
             "graph": bool(args.graph),
             "flush_between_steps_gib": args.flush_gib,
-            "inf_nan_every": args.inject_every,
-            "placement": ("separate allocations" if args.no_arena else
-                          f"one arena, buffer order {shard.placement}"
-                          + (" (fastest of the orders timed at setup)"
-                             if args.placement == "auto" else "")
-                          + f", min gap {args.min_gap_gib:g} GiB"),
+            "inf_nan_every": inject_every,
+            "placement": layout,
+            "placement_search": args.placement == "auto",
             "placement_candidates": len(shard.placement_ms) or None,
             # the finalists' medians of three timed steps (the choice is their minimum)
             "placement_setup_ms": dict(sorted(getattr(shard, "placement_finalists_ms", {}).items(),
@@ -606,7 +620,7 @@ def main():
         "step_frac_of_peak": round(step_bytes / (whole_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "phases": phases,
         "applied_steps": applied,
-        "skipped_steps": args.steps - applied,
+        "skipped_steps": steps - applied,
         "final_loss_scale": shard_scale,
         "per_step_ms": [round(x, 4) for x in per_step],
         "median_step_ms": round(float(np.median(per_step)), 4),
@@ -614,11 +628,72 @@ def main():
         "final_norm": final_norm,
         "host_wall_s": round(wall, 4),
         "roofline": roofline,
+        "_begin": begin,
     }
-    del bufs, shard
+    # drop every reference to the shard's device memory before the next run
+    planted = None
+    del bufs, shard, flush, graph, planted, copy_in, write_back, one_step
+    import gc
+    gc.collect()
     torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "runs on one GPU only: the owner-shard step is "
+                          "measured on one GPU's partition; run with --gpus 1"}), file=sys.stderr)
+        sys.exit(2)
+    if args.steps is None:
+        args.steps = 40 if args.workload == "buckets" else 20
+    if args.inject_every is None:
+        args.inject_every = 4 if args.workload == "buckets" else 0
+    if args.inject_every < 0 or args.inject_every == 1:
+        print(json.dumps({"error": "--inject-every takes 0 (off) or K >= 2, so that some "
+                          "steps run whole"}), file=sys.stderr)
+        sys.exit(2)
+    if args.graph and args.host_control:
+        print(json.dumps({"error": "--graph replays a step with device-resident control; it "
+                          "cannot be combined with --host-control"}), file=sys.stderr)
+        sys.exit(2)
+    if args.write_back and args.workload != "buckets":
+        print(json.dumps({"error": "--write-back applies to --workload buckets"}), file=sys.stderr)
+        sys.exit(2)
+    from synth import workloads as W
+
+    run = run_workload(args, args.workload, args.steps, args.inject_every, calibrate=True)
+    begin = run.pop("_begin")
+    result = {
+        "metric": "params updated/s per GPU (ZeRO shard AdamW step) + achieved HBM GB/s % of peak",
+        "value": run.pop("value"),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": run.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+    }
+    result.update(run)
+    if args.secondary and args.secondary != args.workload:
+        # a second shard in the same run, same options, its own JSON object
+        sec = run_workload(args, args.secondary, args.secondary_steps, 0)
+        sec.pop("_begin")
+        keep = ("value", "ms_per_step", "median_step_ms", "step_GBps", "step_frac_of_peak",
+                "phases", "roofline", "applied_steps", "final_norm", "per_step_ms")
+        result["secondary"] = {"workload": sec["config"]["workload"],
+                               "steps": args.secondary_steps, "unit": "params/s",
+                               **{k: sec[k] for k in keep},
+                               "config": {k: sec["config"][k] for k in
+                                          ("description", "owned_elems", "ranks", "placement",
+                                           "rank_layout", "reduce_windows", "in_place_reduce",
+                                           "placement_search", "arena_slack_gib")}}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, begin, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(W.WORKLOADS[args.workload], begin, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

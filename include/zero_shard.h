@@ -385,6 +385,35 @@ int zero_reduce_check_ranges(void* dst, const void* const* srcs, int32_t n_ranks
                              zero_step_result* res, void* workspace, size_t workspace_bytes,
                              int32_t accumulate, hipStream_t stream);
 
+/* Reduce+check over reduce buckets whose rank contributions arrive in
+ * buffers of their own (ZeRO-2 source walkthrough, section 4.2: gradients are
+ * reduced bucket by bucket of reduce_bucket_size elements, and each bucket's
+ * part of the owner's partition is summed over the N ranks; section 三:
+ * reduce_bucket_size 5e8).  Window w is the owner's slice of one bucket: it
+ * covers dst[windows[w].offset, windows[w].offset + windows[w].count) and
+ * takes rank r's values from srcs[w * n_ranks + r][0 .. count), so each
+ * bucket's N slices can sit wherever they arrived (for example back to back
+ * in one receive buffer per bucket).  The result is that of
+ * zero_reduce_check_owned on each window in list order (accumulate != 0 after
+ * the first), except that sumsq adds the per-block partials of all windows in
+ * one fold, as in zero_reduce_check_ranges.  Windows are not merged: each
+ * non-empty window is one launch of the single-range kernel.
+ *   srcs[n_windows * n_ranks]  host array of device pointers; the pointers of
+ *                              an empty window are not read
+ *   windows[n_windows]         host array, read during the call; disjoint in
+ *                              dst, offsets and counts >= 0 (ZERO_EINVAL;
+ *                              ZERO_ERANGE when offset + count overflows)
+ *   workspace                  at least zero_range_workspace_bytes(windows,
+ *                              n_windows) bytes
+ * Within a window dst may be the same pointer as one of its rank buffers; no
+ * other overlap is allowed.  Every other argument as in
+ * zero_reduce_check_ranges. */
+int zero_reduce_check_buckets(void* dst, const void* const* srcs, int32_t n_ranks,
+                              const zero_range* windows, int32_t n_windows, int32_t dtype,
+                              float inv_scale, const zero_step_control* ctl,
+                              zero_step_result* res, void* workspace, size_t workspace_bytes,
+                              int32_t accumulate, hipStream_t stream);
+
 int zero_adamw_step_ranges(float* master, float* exp_avg, float* exp_avg_sq, void* param16,
                            const void* grad16, const zero_range* ranges, int32_t n_ranges,
                            int32_t dtype, const zero_adamw_hparams* hp,

@@ -3,8 +3,9 @@ range of the flat buffer, on the host (numpy) or on the device (torch tensors
 filled by libsynth_dev).  Both sides give identical bits for every index.
 
 Initial values: weights N(0, 0.02), biases 0, normalisation gains 1.
-Gradients of rank r at step s: N(0, sigma) times the loss scale, one stream per
-(step, rank) over global flat indices; elements past the last tensor (the
+Gradients of rank r at step s: N(0, sigma) times the loss scale (times
+2^-(r * rank_shift) where a workload sets it), one stream per (step, rank)
+over global flat indices; elements past the last tensor (the
 alignment padding) are 0.  Injected inf/NaN go to the index the workload's
 schedule names.
 """
@@ -33,11 +34,11 @@ def host_rank_grads(wl: Workload, step: int, scale: float, begin: int, end: int,
                     padded: int, threads: int = 1, ranks=None, out_bufs=None) -> list:
     """The N ranks' gradients over [begin, end) of the flat buffer
     (written into `out_bufs` when given, one uint16 array per rank)."""
-    spec = wl.grad_spec(scale)
     phi = wl.phi
     inj = injections(wl, padded).get(step)
     out = []
     for k, r in enumerate(range(wl.world) if ranks is None else ranks):
+        spec = wl.grad_spec(scale, r)
         if out_bufs is None:
             g = np.zeros(end - begin, dtype=np.uint16)
         else:
@@ -87,7 +88,7 @@ def device_rank_grad(wl: Workload, step: int, scale: float, rank: int, begin: in
     stream = torch.cuda.current_stream().cuda_stream
     if stop > begin:
         fill_device(raw.data_ptr(), stop - begin, begin, wl.grad_key(step, rank),
-                    wl.grad_spec(scale), stream)
+                    wl.grad_spec(scale, rank), stream)
     if end > max(stop, begin):
         raw[max(stop, begin) - begin:].zero_()
     inj = injections(wl, padded).get(step)

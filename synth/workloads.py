@@ -42,6 +42,7 @@ class Workload:
     owners: str = "first"                    # "first": owner 0 only; "all": every owner
     bucket_cap: Optional[int] = None         # reduce bucket size, elements
     inject_every: int = 0                    # inject inf/NaN every k-th step (1-based)
+    rank_shift: int = 0                      # rank r's draw is scaled by 2^-(r * rank_shift)
     seed: int = 1
     description: str = ""
 
@@ -53,9 +54,13 @@ class Workload:
     def phi(self) -> int:
         return int(sum(t[1] for t in self.tensors))
 
-    def grad_spec(self, scale: float) -> NormalSpec:
+    def grad_spec(self, scale: float, rank: int = 0) -> NormalSpec:
+        """The draw of rank `rank`'s gradient at loss scale `scale`.  With
+        rank_shift the ranks' values sit on binary grids rank_shift binades
+        apart, so their sums in fp32 are no longer exact."""
         base = normal_spec(self.grad_sigma, self.dtype)
-        return scaled(base, scale) if scale != 1.0 else base
+        factor = scale * 2.0 ** (-rank * self.rank_shift)
+        return scaled(base, factor) if factor != 1.0 else base
 
     def init_spec(self) -> NormalSpec:
         return normal_spec(self.init_sigma, self.dtype)
@@ -152,14 +157,15 @@ def _make() -> dict:
                     "vocab 30522), N=8, fp16 grads, clip 1.0")
     w["llama7b"] = Workload(
         name="llama7b", tensors=llama_tensors(4096, 32, 11008), world=8, dtype=BF16,
-        grad_sigma=1e-4, steps=5, clip=1.0, seed=3,
+        grad_sigma=1e-4, steps=5, clip=1.0, bucket_cap=500_000_000, seed=3,
         description="LLaMA-7B-shaped flat buffer (32 layers, d=4096, FFN 11008, vocab 32000), "
-                    "N=8, bf16 grads N(0,1e-4), clip 1.0")
+                    "N=8, bf16 grads N(0,1e-4), clip 1.0, 5e8-element reduce buckets")
     w["llama70b"] = Workload(
         name="llama70b", tensors=llama_tensors(8192, 80, 28672, kv_dim=1024), world=8,
-        dtype=BF16, grad_sigma=1e-4, steps=3, clip=1.0, seed=4,
+        dtype=BF16, grad_sigma=1e-4, steps=3, clip=1.0, bucket_cap=500_000_000, seed=4,
         description="LLaMA-70B-shaped flat buffer (80 layers, d=8192, FFN 28672, GQA 8 KV heads, "
-                    "vocab 32000), N=8, bf16 grads N(0,1e-4), clip 1.0, in-place reduce")
+                    "vocab 32000), N=8, bf16 grads N(0,1e-4), clip 1.0, 5e8-element reduce "
+                    "buckets")
     w["buckets"] = Workload(
         name="buckets", tensors=bucket_tensors(), world=16, dtype=FP16, grad_sigma=1e-3,
         steps=40, scale0=2.0 ** 16, dynamic=True, owners="all", bucket_cap=500_000_000,
@@ -173,6 +179,13 @@ def _make() -> dict:
         bucket_cap=400_000, inject_every=4, seed=6,
         description="400 tensors log-uniform in [64, 2^14] in 4e5-element reduce buckets, "
                     "N=16, dynamic loss scale, inf/NaN every 4th step")
+    # ToyModel whose ranks' gradients sit on grids 3 binades apart (rank 7's
+    # values are 2^-21 times rank 0's): the fp32 sums of the reduce round
+    w["toy_offgrid"] = Workload(
+        name="toy_offgrid", tensors=toy_tensors(), world=8, dtype=FP16, grad_sigma=1e-3,
+        steps=3, scale0=2.0 ** 16, dynamic=True, rank_shift=3, seed=11,
+        description="ToyModel flat buffer, N=8, fp16 grads N(0,1e-3)x2^16x2^-3r for rank r "
+                    "(off one common grid)")
     w["toy_tiny"] = Workload(
         name="toy_tiny", tensors=toy_tensors(hidden=64, layers=2, classes=10), world=8,
         dtype=FP16, grad_sigma=1e-3, steps=3, scale0=2.0 ** 16, dynamic=True, seed=9,

@@ -163,28 +163,39 @@ def test_builder_loads_without_the_package():
     assert r.returncode == 0, r.stderr
 
 
-@pytest.mark.parametrize("n_ranks,in_place", [(0, None), (1, 0), (8, None), (8, 0), (8, 5),
-                                              (16, None), (16, 15)])
-def test_arena_orders_place_every_buffer_once(n_ranks, in_place):
+@pytest.mark.parametrize("n_ranks,in_place,bucket", [(0, None, False), (1, 0, False),
+                                                     (8, None, False), (8, 0, False),
+                                                     (8, 5, False), (16, None, False),
+                                                     (16, 15, False), (8, None, True)])
+def test_arena_orders_place_every_buffer_once(n_ranks, in_place, bucket):
     """Every arena order is a permutation of the step's buffers, and the
     placement gives each one a 64 KiB aligned, non-overlapping range, with
-    the AdamW arrays at least min_gap apart."""
-    from zero_partitioned_mixed_shard_amd.shard import ARENA_ORDERS, ShardStep
-    names = ["master", "exp_avg", "exp_avg_sq", "param16"] + (["red"] if in_place is None else [])
-    names += [f"rank{r}" for r in range(n_ranks)]
-    streams = set(names[:4]) | ({"red"} if in_place is None else {f"rank{in_place}"})
-    kinds = {nm: (None, 4 if nm in ("master", "exp_avg", "exp_avg_sq") else 2) for nm in names}
+    master, m and v at least min_gap apart.  With the bucket layout the
+    rank data are blocks of different sizes, one per reduce window, kept in
+    window order."""
+    from zero_partitioned_mixed_shard_amd.shard import ARENA_ORDERS, FP32_ARRAYS, ShardStep
     n = 1_000_003
+    names = ["master", "exp_avg", "exp_avg_sq", "param16"] + (["red"] if in_place is None else [])
+    sizes = {nm: n * (4 if nm in FP32_ARRAYS else 2) for nm in names}
+    rank_names = ([f"rankw{w}" for w in range(12)] if bucket else
+                  [f"rank{r}" for r in range(n_ranks)])
+    for k, nm in enumerate(rank_names):
+        sizes[nm] = n_ranks * (1000 + 77777 * k) * 2 if bucket else 2 * n
+    names += rank_names
+    streams = set(names[:4]) | ({"red"} if in_place is None else {f"rank{in_place}"})
     for name, order in ARENA_ORDERS.items():
         seq = order(names, streams, in_place)
         assert sorted(seq) == sorted(names), name
+        if bucket:
+            assert [nm for nm in seq if nm.startswith("rank")] == rank_names, name
+        gap_set = set(FP32_ARRAYS)
         for gap in (0, 3 << 20):
-            offs, end = ShardStep._place(seq, kinds, streams, n, gap)
-            spans = sorted((offs[nm], offs[nm] + n * kinds[nm][1]) for nm in names)
+            offs, end = ShardStep._place(seq, sizes, gap_set, gap)
+            spans = sorted((offs[nm], offs[nm] + sizes[nm]) for nm in names)
             assert all(a % (1 << 16) == 0 for a, _ in spans)
             assert all(b <= c for (_, b), (c, _) in zip(spans, spans[1:])), name
             assert spans[-1][1] == end
-            st = sorted(offs[nm] for nm in streams)
+            st = sorted(offs[nm] for nm in gap_set)
             assert all(b - a >= gap for a, b in zip(st, st[1:])), name
 
 
@@ -231,6 +242,46 @@ def test_range_lists_are_checked_before_launching():
         Z.zero_check_workspace_bytes(10_000_019)
     assert Z.zero_range_workspace_bytes([(0, 4096), (4096, 4096)]) >= \
         Z.zero_check_workspace_bytes(8192)
+
+
+def test_bucket_windows_are_checked_before_launching():
+    """zero_reduce_check_buckets rejects bad windows on the host like the
+    range-list calls, and a missing rank pointer of a non-empty window
+    (ZERO_EINVAL); the pointers of an empty window are not read."""
+    import ctypes
+    L = Z.lib()
+    fake = ctypes.c_void_p(0x10000)          # never dereferenced: every call fails first
+    bad = {
+        "negative offset": ([(-1, 4)], Z.ZERO_EINVAL),
+        "negative count": ([(0, -4)], Z.ZERO_EINVAL),
+        "overlap": ([(0, 100), (99, 10)], Z.ZERO_EINVAL),
+        "overflow": ([(2 ** 62, 2 ** 62)], Z.ZERO_ERANGE),
+    }
+    for what, (rs, want) in bad.items():
+        srcs = (ctypes.c_void_p * (2 * len(rs)))(*([fake] * (2 * len(rs))))
+        got = L.zero_reduce_check_buckets(fake, srcs, 2, Z._ranges(rs), len(rs), Z.ZERO_BF16, 1.0,
+                                          None, fake, fake, 1 << 30, 0, None)
+        assert got == want, what
+    ok = Z._ranges([(0, 10), (10, 0), (20, 5)])
+    # window 2's second rank is missing
+    srcs = (ctypes.c_void_p * 6)(fake, fake, None, None, fake, None)
+    assert L.zero_reduce_check_buckets(fake, srcs, 2, ok, 3, Z.ZERO_BF16, 1.0, None, fake, fake,
+                                       1 << 30, 0, None) == Z.ZERO_EINVAL
+    srcs = (ctypes.c_void_p * 6)(fake, fake, None, None, fake, fake)
+    for args, what in (((None, srcs, 2, ok, 3, Z.ZERO_BF16, 1.0, None, fake, fake, 1 << 30),
+                        "no dst"),
+                       ((fake, None, 2, ok, 3, Z.ZERO_BF16, 1.0, None, fake, fake, 1 << 30),
+                        "no rank pointers"),
+                       ((fake, srcs, 0, ok, 3, Z.ZERO_BF16, 1.0, None, fake, fake, 1 << 30),
+                        "no ranks"),
+                       ((fake, srcs, 2, ok, 3, 7, 1.0, None, fake, fake, 1 << 30), "dtype"),
+                       ((fake, srcs, 2, ok, 3, Z.ZERO_BF16, 0.0, None, fake, fake, 1 << 30),
+                        "inv_scale"),
+                       ((fake, srcs, 2, ok, 3, Z.ZERO_BF16, 1.0, None, None, fake, 1 << 30),
+                        "no result"),
+                       ((fake, srcs, 2, ok, 3, Z.ZERO_BF16, 1.0, None, fake, fake, 8),
+                        "workspace too small")):
+        assert L.zero_reduce_check_buckets(*args, 0, None) == Z.ZERO_EINVAL, what
 
 
 def test_header_compiles_as_c(tmp_path):

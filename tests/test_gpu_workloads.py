@@ -9,6 +9,8 @@ bit-equal or within 2e-6 relative, the 16-bit copy within 1 ulp, and the loss
 scale and step count equal.  Inputs are regenerated on each side from the
 same seeded generator.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -51,20 +53,26 @@ def _setup(wl, owner_ids, round_robin=False):
 
 def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=False,
                device_control=False, placement=None, in_place_rank=None, arena_slack=0,
-               batched=True):
+               batched=True, rank_layout="flat", bucket_cap=None):
     """placement: None for separate rank buffers handed to each step, else
-    the arena order of a step that holds its own rank buffers."""
+    the arena order of a step that holds its own rank data.  rank_layout
+    "bucket": the step holds its own rank data, each reduce window's N slices
+    back to back (reduce windows from the workload's buckets, or from
+    bucket_cap)."""
     wl = W.WORKLOADS[name]
+    if bucket_cap is not None:
+        wl = dataclasses.replace(wl, bucket_cap=bucket_cap)
     steps = wl.steps if steps is None else steps
     offs, padded, owners, begin, end, windows = _setup(wl, owner_ids, round_robin)
+    bucket = rank_layout == "bucket"
     arena = placement is not None
     shard = ShardStep(begin, end, owners, wl.dtype, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2,
                       eps=wl.eps, weight_decay=wl.weight_decay, max_grad_norm=wl.clip,
                       scale0=wl.scale0, min_scale=wl.min_scale, window=wl.window, windows=windows,
-                      fused=fused, device_control=device_control, own_ranks=arena,
-                      world=wl.world if arena else 0, arena=arena,
+                      fused=fused, device_control=device_control, own_ranks=arena or bucket,
+                      world=wl.world if arena or bucket else 0, arena=arena,
                       placement=placement or "interleaved", in_place_rank=in_place_rank,
-                      arena_slack=arena_slack, batched=batched)
+                      arena_slack=arena_slack, batched=batched, rank_layout=rank_layout)
     # initial state: device generator on the GPU, host generator for the oracle
     d_p16 = I.device_param16(wl, offs, begin, end)
     h_p16 = I.host_param16(wl, offs, begin, end, threads)
@@ -74,13 +82,20 @@ def run_parity(name, owner_ids, steps=None, threads=4, fused=True, round_robin=F
               for a, b in owners]
     scaler = oracle.Scaler(wl.scale0, wl.min_scale, wl.window)
     t = 0
-    rank_bufs = shard.rank_bufs if arena else \
-        [torch.empty(end - begin, dtype=shard.tdtype, device="cuda") for _ in range(wl.world)]
+    if bucket:
+        rank_bufs = None
+    else:
+        rank_bufs = shard.rank_bufs if arena else \
+            [torch.empty(end - begin, dtype=shard.tdtype, device="cuda") for _ in range(wl.world)]
     skipped = 0
     for s in range(1, steps + 1):
         assert shard.scale == scaler.scale
-        for r in range(wl.world):
-            I.device_rank_grad(wl, s, scaler.scale, r, begin, end, padded, out=rank_bufs[r])
+        if bucket:
+            shard.fill_ranks(lambda r, a, b, out: I.device_rank_grad(
+                wl, s, scaler.scale, r, begin + a, begin + b, padded, out=out))
+        else:
+            for r in range(wl.world):
+                I.device_rank_grad(wl, s, scaler.scale, r, begin, end, padded, out=rank_bufs[r])
         info = shard.step(rank_bufs)
         host = I.host_rank_grads(wl, s, scaler.scale, begin, end, padded, threads)
         per_owner = [[g[a - begin:b - begin] for g in host] for a, b in owners]
@@ -121,6 +136,44 @@ def test_toy_last_owner_with_padding():
 
 def test_bert_owner0_all_steps_clip():
     run_parity("bert", [0])
+
+
+def _fp32_inexact_fraction(wl, step, scale, begin, n):
+    """Fraction of the first n columns whose rank-order fp32 sum differs from
+    the exact sum (the reduce's rounding then matters)."""
+    _, _, padded = oracle.layout(wl.numels, wl.world, wl.align)
+    host = I.host_rank_grads(wl, step, scale, begin, begin + n, padded)
+    vals = [oracle.decode16(g, wl.dtype).astype(np.float64) for g in host]
+    acc = np.zeros(n, np.float32)
+    for v in vals:
+        acc = (acc + v.astype(np.float32)).astype(np.float32)
+    exact = np.sum(vals, axis=0)            # exact: binary16 values, 8 ranks, 32 binades
+    return float(np.mean(acc.astype(np.float64) != exact))
+
+
+def test_toy_offgrid_owner0_rank_order_rounding():
+    """The ranks' gradients on grids 3 binades apart (rank 7's values 2^-21
+    times rank 0's): most fp32 sums of the reduce round, so the rank order
+    and the fp32 reading of the reduce are exercised on every element of a
+    whole workload run, whose results still match the oracle's bit for bit
+    (reduced gradient) and to the usual tolerances."""
+    wl = W.WORKLOADS["toy_offgrid"]
+    assert _fp32_inexact_fraction(wl, 1, wl.scale0, 0, 1 << 16) > 0.5
+    run_parity("toy_offgrid", [0])
+
+
+@pytest.mark.parametrize("name,owners,cap,placement", [
+    ("toy", [0], 3_000_000, None), ("toy", [0], 3_000_000, "spread"),
+    ("toy_offgrid", [2], 5_000_000, "spread"),
+    ("buckets_small", list(range(16)), None, "spread")])
+def test_bucket_rank_layout(name, owners, cap, placement):
+    """The ranks' gradients held bucket by bucket (each reduce window's N
+    slices back to back) and reduced with one zero_reduce_check_buckets call:
+    tensor-aligned buckets of the ToyModel (8 ranks, the LDS-staged reduce)
+    and the fragmented 400-tensor group with all 16 owners and inf/NaN steps,
+    in separate allocations and in the spread arena."""
+    run_parity(name, owners, steps=4, placement=placement, rank_layout="bucket", bucket_cap=cap,
+               device_control=name == "buckets_small")
 
 
 @pytest.mark.parametrize("name,owner,batched", [("toy", 0, True), ("toy", 5, True),

@@ -65,6 +65,7 @@ EXPORTS = (
     "zero_step_control_init", "zero_reduce_check_owned_ctl", "zero_unscale_check_norm_ctl",
     "zero_adamw_step_ctl", "zero_step_control_update",
     "zero_range_workspace_bytes", "zero_reduce_check_ranges", "zero_adamw_step_ranges",
+    "zero_reduce_check_buckets",
 )
 
 
@@ -119,6 +120,8 @@ def _load():
         "zero_reduce_check_ranges": ([P, P, i32, P, i32, i32, f32, P, P, P, ctypes.c_size_t, i32, P],
                                      ctypes.c_int),
         "zero_adamw_step_ranges": ([P, P, P, P, P, P, i32, i32, P, P, P, P], ctypes.c_int),
+        "zero_reduce_check_buckets": ([P, P, i32, P, i32, i32, f32, P, P, P, ctypes.c_size_t, i32,
+                                       P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -470,3 +473,33 @@ def zero_adamw_step_ranges(master, exp_avg, exp_avg_sq, param16, grad16, ranges:
         _dev(grad16, 2, need, "grad16"), _ranges(ranges), len(ranges), dt, ctypes.byref(hp),
         _ctl(ctl_dev) if ctl_dev is not None else None, res.data_ptr(), _stream(stream)),
         "zero_adamw_step_ranges")
+
+
+def zero_reduce_check_buckets(dst, windows: Sequence, srcs: Sequence[Sequence], inv_scale: float,
+                              res, workspace, accumulate: bool = False, ctl_dev=None,
+                              stream=None) -> None:
+    """windows: (offset, count) pairs of elements of dst; srcs[w]: the N rank
+    tensors of window w, each holding at least its count elements."""
+    if len(srcs) != len(windows):
+        raise ValueError("one list of rank tensors per window")
+    n_ranks = len(srcs[0]) if srcs else 1
+    if not 1 <= n_ranks <= ZERO_MAX_RANKS:
+        raise ValueError("1..16 rank buffers")
+    dt = _dtype_code(dst)
+    flat = []
+    for (a, c), ranks in zip(windows, srcs):
+        if len(ranks) != n_ranks:
+            raise ValueError("every window needs the same number of rank tensors")
+        for t in ranks:
+            if _dtype_code(t) != dt:
+                raise TypeError("rank buffers and dst must share the 16-bit type")
+            flat.append(_dev(t, 2, int(c), "src") if int(c) > 0 else None)
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    ptrs = (ctypes.c_void_p * max(1, len(flat)))(*flat)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.zero_reduce_check_buckets(
+        _dev(dst, 2, _extent(windows), "dst"), ptrs, n_ranks, _ranges(windows), len(windows), dt,
+        float(inv_scale), _ctl(ctl_dev) if ctl_dev is not None else None, res.data_ptr(),
+        _dev(workspace, workspace.element_size(), 0, "workspace"), ws_bytes,
+        int(bool(accumulate)), _stream(stream)), "zero_reduce_check_buckets")

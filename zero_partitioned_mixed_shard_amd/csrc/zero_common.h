@@ -29,6 +29,7 @@ constexpr int64_t kMaxLaunchBlocks = (int64_t(1) << 32) / kThreads - 1;
 constexpr unsigned kLdsPerCU = 160 * 1024;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -66,6 +67,16 @@ __device__ __forceinline__ f32x4 load_f4(const float* p) {
 }
 __device__ __forceinline__ void store_f4(float* p, f32x4 v) {
     *reinterpret_cast<f32x4*>(p) = v;
+}
+// One wave instruction of a direct global -> LDS copy (gfx950
+// global_load_lds_dwordx4): lane l moves the 16 bytes at its own `src` to
+// lds + 16 l, so 64 lanes fill 1 KiB of LDS without going through VGPRs.
+// `lds` must be the same for every lane of the wave.  NT selects a
+// non-temporal (streaming) load.  The data may be read from LDS once the
+// wave's vector-memory counter has drained.
+template <bool NT>
+__device__ __forceinline__ void load_to_lds(const void* src, char* lds) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, NT ? 2 : 0);
 }
 __device__ __forceinline__ uint16_t half_of(u32x4 w, int k) {
     return (uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu));

@@ -172,6 +172,24 @@ __device__ __forceinline__ void reduce_tile(const u32x4 (&w)[NR], uint16_t* d, f
 // 2 blocks per CU, 16 ranks 5.70 -> 5.88 TB/s with 1).
 constexpr int kReduceTiles = 2;
 constexpr int reduce_blocks_per_cu(int nr) { return nr >= 16 ? 1 : (16 / nr > 8 ? 8 : 16 / nr); }
+// Elements of one reduce block, and the rank count whose whole blocks stage
+// their rank data in LDS (reduce_block_lds): 8 ranks x 8 KiB = 64 KiB per
+// block, two blocks per CU.  On MI355X that ran 4.4-4.9 % faster than
+// loading into registers at the LLaMA-7B shard size and 1.8-2.0 % at the
+// 70B size (same placements, A/B); at 1-6 ranks it made no difference and at
+// 12-16 ranks (one block per CU) it was 7 % slower.
+constexpr int kReduceBlockElems = kReduceTiles * kTile;
+constexpr int kLdsRanks = 8;
+constexpr unsigned kReduceLdsBytes = kLdsRanks * kReduceBlockElems * 2;
+// Dynamic LDS of a reduce launch over nr ranks: the occupancy cap, or for
+// the LDS-staged rank count its staging buffer (64 KiB, which leaves room for
+// the same two blocks per CU).
+inline unsigned reduce_lds(int nr) {
+    const unsigned cap = lds_for_blocks(reduce_blocks_per_cu(nr));
+    return nr == kLdsRanks && kReduceLdsBytes > cap ? kReduceLdsBytes : cap;
+}
+static_assert(2 * kReduceLdsBytes <= kLdsPerCU && 3 * kReduceLdsBytes > kLdsPerCU,
+              "the 8-rank staging buffer keeps two blocks per CU");
 
 // Reduce of NR ranks; with CHECK also the overflow flag and squared norm of
 // the reduced values, one partial per block.  Block b owns kReduceTiles
@@ -179,6 +197,43 @@ constexpr int reduce_blocks_per_cu(int nr) { return nr >= 16 ? 1 : (16 / nr > 8 
 // x NR 128-bit words) before any arithmetic.  No __restrict__ on dst / src:
 // dst may be one of the sources (every element is read, then written, by
 // the same lane).
+// A whole block of the 8-rank reduce with the rank data staged in LDS: each
+// wave copies two 1 KiB chunks of every rank straight into LDS (rank-major
+// issue order), the block waits for all of them, then every lane reduces the
+// same two lane tiles as in the register path (elements 8t and 2048 + 8t of
+// the block for lane t), in the same order, so the sums, the stored values
+// and the block's partial are bit-identical to that path.
+template <int DT, bool CHECK>
+__device__ __forceinline__ void reduce_block_lds(uint16_t* dst, const RankPtrs& src, int64_t e0,
+                                                 float& inv, const zero_step_control* ctl,
+                                                 double& sq, uint32_t& bad) {
+    extern __shared__ __attribute__((aligned(16))) char stage[];   // kReduceLdsBytes
+    constexpr int kChunk = 512;                                     // elements per wave copy
+    constexpr int kChunks = kReduceBlockElems / kChunk;             // per rank
+    constexpr int kWaves = kThreads / 64;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < kLdsRanks; ++r)
+#pragma unroll
+        for (int j = 0; j < kChunks / kWaves; ++j) {
+            const int ch = w + kWaves * j;
+            load_to_lds<true>(src.p[r] + e0 + ch * kChunk + lane * kVec,
+                              stage + (r * kChunks + ch) * (kChunk * 2));
+        }
+    if (CHECK && ctl) inv = ctl->inv_scale;         // while the copies are in flight
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kReduceTiles; ++t) {
+        const int q = t * kThreads + threadIdx.x;   // lane tile within the block
+        u32x4 w8[kLdsRanks];
+#pragma unroll
+        for (int r = 0; r < kLdsRanks; ++r)
+            w8[r] = *reinterpret_cast<const u32x4*>(stage + r * (kReduceBlockElems * 2) + q * 16);
+        reduce_tile<DT, kLdsRanks, CHECK>(w8, dst + e0 + q * kVec, inv, sq, bad);
+    }
+}
+
 template <int DT, int NR, bool CHECK>
 __device__ __forceinline__ void reduce_block(uint16_t* dst, const RankPtrs& src, const Split& s,
                                              float inv, const zero_step_control* ctl,
@@ -190,7 +245,10 @@ __device__ __forceinline__ void reduce_block(uint16_t* dst, const RankPtrs& src,
     // rank loads are issued: read before them, its scalar-load latency would
     // sit in front of every block's HBM loads.
     if (s.aligned) {
-        if (lane_tile<kReduceTiles>(s, kReduceTiles - 1) < s.nvec) {   // every row in range
+        if (NR == kLdsRanks && (blk + 1) * (kReduceTiles * kThreads) <= s.nvec) {  // whole block
+            reduce_block_lds<DT, CHECK>(dst, src, s.head + blk * kReduceBlockElems, inv, ctl, sq,
+                                        bad);
+        } else if (lane_tile<kReduceTiles>(s, kReduceTiles - 1) < s.nvec) {   // every row in range
             u32x4 w[kReduceTiles][NR];
 #pragma unroll
             for (int t = 0; t < kReduceTiles; ++t) {
@@ -439,11 +497,72 @@ __device__ __forceinline__ void adam_quads(const AdamConsts& c0, const zero_step
     }
 }
 
-// Lane l of a block takes the quads at 4l and kTile/2 + 4l of the block's
-// kTile elements, so every fp32 access instruction of a wave covers 1 KiB
-// contiguously and the 16-bit streams 512 B.  (Eight consecutive elements
-// per lane, i.e. two 16-byte fp32 accesses 16 bytes apart that each fill
-// half of every cache line, measured 2% slower on the LLaMA-70B shard.)
+// A whole AdamW block with each wave's inputs staged in LDS: wave w owns the
+// 512 consecutive elements at e0 + 512 w and copies its gradient (1 KiB) and
+// master / m / v (2 KiB each) straight into its own 7 KiB of LDS, then its
+// lane l updates the quads at 4l and 256 + 4l of those elements.  No block
+// barrier: a wave reads only what it copied, once its own copies have
+// landed, so the waves of a block run independently.  On MI355X this ran
+// 0.3-1.8 % faster than the register path (LLaMA-7B and 70B shard sizes,
+// several layouts, A/B); the per-element arithmetic is the same, so the
+// results are bit-identical.
+constexpr int kAdamWaveElems = kTile / (kThreads / 64);        // 512
+constexpr int kAdamWaveBytes = kAdamWaveElems * (2 + 3 * 4);   // 7 KiB
+
+template <int DT>
+__device__ __forceinline__ void adam_block_lds(const AdamConsts& c0, const zero_step_control* ctl,
+                                               const zero_step_result* res, float* master,
+                                               float* ma, float* va, uint16_t* p16,
+                                               const uint16_t* g16, int64_t e0) {
+    extern __shared__ __attribute__((aligned(16))) char stage[];   // kThreads / 64 waves
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t e = e0 + (int64_t)w * kAdamWaveElems;
+    char* lg = stage + w * kAdamWaveBytes;                         // 16-bit gradient, 1 KiB
+    char* lp = lg + kAdamWaveElems * 2;                            // master, 2 KiB
+    char* lm = lp + kAdamWaveElems * 4;                            // m
+    char* lv = lm + kAdamWaveElems * 4;                            // v
+    load_to_lds<true>(g16 + e + lane * 8, lg);                    // read once: non-temporal
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t o = e + j * 256 + lane * 4;
+        load_to_lds<false>(master + o, lp + j * 1024);
+        load_to_lds<false>(ma + o, lm + j * 1024);
+        load_to_lds<false>(va + o, lv + j * 1024);
+    }
+    // the step's scalars while the copies are in flight
+    const AdamConsts c = step_consts(c0, ctl);
+    const float inv = res->inv_scale, coef = clip_coef(c, res);
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = lane + 64 * j;                               // quad of the wave's elements
+        const u32x2 gw = *reinterpret_cast<const u32x2*>(lg + q * 8);
+        f32x4 p = *reinterpret_cast<const f32x4*>(lp + q * 16);
+        f32x4 m = *reinterpret_cast<const f32x4*>(lm + q * 16);
+        f32x4 v = *reinterpret_cast<const f32x4*>(lv + q * 16);
+        uint16_t ph[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float g = to_f32<DT>(half_of2(gw, k)) * inv;
+            g = g * coef;
+            const AdamElem o = adam_update(c, g, p[k], m[k], v[k]);
+            p[k] = o.p;
+            m[k] = o.m;
+            v[k] = o.v;
+            ph[k] = from_f32<DT>(o.p);
+        }
+        const int64_t x = e + 4 * q;
+        store_f4(master + x, p);
+        store_f4(ma + x, m);
+        store_f4(va + x, v);
+        store_nt_b64(p16 + x, pack4(ph));                          // written once: non-temporal
+    }
+}
+
+// Blocks that lie wholly inside the vector body take adam_block_lds.  In the
+// last, partial block lane l takes the quads at 4l and kTile/2 + 4l of the
+// block's kTile elements, so every fp32 access instruction of a wave covers
+// 1 KiB contiguously and the 16-bit streams 512 B.
 template <int DT>
 __device__ __forceinline__ void adamw_block(float* __restrict__ master, float* __restrict__ ma,
                                             float* __restrict__ va, uint16_t* __restrict__ p16,
@@ -463,9 +582,12 @@ __device__ __forceinline__ void adamw_block(float* __restrict__ master, float* _
     // quads are offsets into the vector body [head, head + 8 nvec), whose
     // length is a multiple of 8: a quad lies wholly inside it or outside
     const int64_t body = s.nvec * kVec;
-    const int64_t o0 = block_id(s) * kTile + 4 * threadIdx.x;
+    const int64_t b0 = block_id(s) * kTile;
+    const int64_t o0 = b0 + 4 * threadIdx.x;
     const int64_t o1 = o0 + kTile / 2;
-    if (o1 < body) {
+    if (b0 + kTile <= body) {
+        adam_block_lds<DT>(c0, ctl, res, master, ma, va, p16, g16, s.head + b0);
+    } else if (o1 < body) {
         const int64_t e[2] = {s.head + o0, s.head + o1};
         adam_quads<DT, 2>(c0, ctl, res, master, ma, va, p16, g16, e);
     } else if (o0 < body) {
@@ -574,8 +696,8 @@ int launch_reduce_n(uint16_t* dst, const RankPtrs& src, int n, const Split& s, f
 #define ZERO_REDUCE_CASE(K)                                                                    \
     case K:                                                                                    \
         return launch_pieces(s, blocks, [&](const Split& piece, int64_t g) {                   \
-            return launch(reduce_kernel<DT, K, CHECK>, g, lds_for_blocks(reduce_blocks_per_cu(K)), \
-                          stream, dst, src, piece, inv, ctl, ps, pf);                          \
+            return launch(reduce_kernel<DT, K, CHECK>, g, reduce_lds(K), stream, dst, src, piece, \
+                          inv, ctl, ps, pf);                                                   \
         });
     switch (n) {
         ZERO_REDUCE_CASE(1) ZERO_REDUCE_CASE(2) ZERO_REDUCE_CASE(3) ZERO_REDUCE_CASE(4)
@@ -686,6 +808,8 @@ AdamConsts adam_consts(const zero_adamw_hparams* hp, bool ctl) {
 // 2 resident blocks per CU: 6.10 -> 6.37 TB/s on the LLaMA-70B-shaped shard,
 // 5.33 -> 5.84 TB/s on the 7B one (MI355X)
 constexpr int kAdamBlocksPerCU = 2;
+static_assert((kThreads / 64) * kAdamWaveBytes <= kLdsPerCU / (kAdamBlocksPerCU + 1) + 2048u,
+              "the AdamW cap's dynamic LDS holds every wave's staging area");
 
 template <int DT>
 int launch_adamw(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* p16,
@@ -768,62 +892,50 @@ int64_t ranges_max_blocks(const zero_range* ranges, int32_t n) {
 }
 
 // Reduce+check over a list of ranges: each range is one launch of the
-// single-range kernel (in pieces past one grid's size), its block partials
-// written after the previous ranges' (range r's first partial at the sum of
-// the earlier ranges' block counts), so the norm of all ranges is folded
-// once.  (Packing several ranges into one launch made every block look up
-// its range before its first load; the dependent scalar loads cost 2-4 %.)
+// single-range kernel (in pieces past one grid's size) reading its ranks at
+// rp[r], its block partials written after the previous ranges' (range r's
+// first partial at the sum of the earlier ranges' block counts), so the norm
+// of all ranges is folded once.  (Packing several ranges into one launch
+// made every block look up its range before its first load; the dependent
+// scalar loads cost 2-4 %.)
 template <int DT>
-int reduce_check_ranges_t(uint16_t* dst, const RankPtrs& rp, int32_t n_ranks,
+int reduce_check_ranges_t(uint16_t* dst, const std::vector<RankPtrs>& rp, int32_t n_ranks,
                           const zero_range* ranges, int32_t n, float inv,
                           const zero_step_control* ctl, double* ps, uint32_t* pf,
                           const std::vector<Split>& splits, const std::vector<int64_t>& blocks,
                           hipStream_t stream) {
     int64_t base = 0;
     for (int32_t r = 0; r < n; ++r) {
-        const int64_t off = ranges[r].offset;
-        RankPtrs sr = rp;
-        for (int k = 0; k < n_ranks; ++k) sr.p[k] = rp.p[k] + off;
-        const int rc = launch_reduce_n<DT, true>(dst + off, sr, n_ranks, splits[r], inv, ctl,
-                                                 ps + base, pf + base, stream);
+        const int rc = launch_reduce_n<DT, true>(dst + ranges[r].offset, rp[r], n_ranks, splits[r],
+                                                 inv, ctl, ps + base, pf + base, stream);
         if (rc != ZERO_OK) return rc;
         base += blocks[r];
     }
     return ZERO_OK;
 }
 
-int reduce_check_ranges_impl(void* dst, const void* const* srcs, int32_t n_ranks,
-                             const zero_range* ranges, int32_t n, int32_t dtype, float inv_scale,
-                             const zero_step_control* ctl, zero_step_result* res, void* workspace,
-                             size_t workspace_bytes, int32_t accumulate, hipStream_t stream) {
+// Checks of the arguments the range-list reduce calls share.
+int reduce_list_args(int32_t n_ranks, int32_t dtype, const void* srcs, float inv_scale,
+                     const zero_step_result* res, const void* workspace) {
     if (n_ranks < 1 || n_ranks > ZERO_MAX_RANKS || !valid_dtype(dtype) || !srcs) return ZERO_EINVAL;
-    bool any = false;
-    int rc = check_ranges(ranges, n, &any);
-    if (rc != ZERO_OK) return rc;
-    if (any && !dst) return ZERO_EINVAL;
-    RankPtrs rp;
-    for (int r = 0; r < ZERO_MAX_RANKS; ++r) rp.p[r] = nullptr;
-    for (int r = 0; r < n_ranks; ++r) {
-        if (any && !srcs[r]) return ZERO_EINVAL;
-        rp.p[r] = (const uint16_t*)srcs[r];
-    }
     if (!res || !workspace || ((uintptr_t)workspace & 7) != 0) return ZERO_EINVAL;
     if (!(inv_scale > 0.0f) || !__builtin_isfinite(inv_scale)) return ZERO_EINVAL;
-    if (workspace_bytes < levels_for(ranges_max_blocks(ranges, n)).bytes) return ZERO_EINVAL;
-    // empty ranges take no blocks and touching ones are merged (with no
-    // elements at all only the result is written, or left as it is when
-    // accumulating); the workspace bound above holds for the merged list
-    const std::vector<zero_range> rs = merged_ranges(ranges, n);
+    return ZERO_OK;
+}
+
+// Launches the ranges (each with its own rank pointers) and folds the norm.
+int reduce_check_list(uint16_t* d, const std::vector<RankPtrs>& rps,
+                      const std::vector<zero_range>& rs, int32_t n_ranks, int32_t dtype,
+                      float inv_scale, const zero_step_control* ctl, zero_step_result* res,
+                      void* workspace, int32_t accumulate, hipStream_t stream) {
     std::vector<Split> splits;
     std::vector<int64_t> blocks;
     int64_t total = 0;
-    uint16_t* d = (uint16_t*)dst;
-    for (const zero_range& rg : rs) {
-        const int64_t off = rg.offset;
+    for (size_t w = 0; w < rs.size(); ++w) {
         const void* all16[ZERO_MAX_RANKS + 1];
-        for (int k = 0; k < n_ranks; ++k) all16[k] = rp.p[k] + off;
-        all16[n_ranks] = d + off;
-        splits.push_back(split_for(vector_head(all16, n_ranks + 1, nullptr, 0), rg.count));
+        for (int k = 0; k < n_ranks; ++k) all16[k] = rps[w].p[k];
+        all16[n_ranks] = d + rs[w].offset;
+        splits.push_back(split_for(vector_head(all16, n_ranks + 1, nullptr, 0), rs[w].count));
         blocks.push_back(tile_blocks(splits.back(), kReduceTiles));
         total += blocks.back();
     }
@@ -832,13 +944,75 @@ int reduce_check_ranges_impl(void* dst, const void* const* srcs, int32_t n_ranks
     char* ws = (char*)workspace;
     double* ps = (double*)(ws + L.sum_off[0]);
     uint32_t* pf = (uint32_t*)(ws + L.flag_off[0]);
-    rc = dtype == ZERO_FP16
-             ? reduce_check_ranges_t<ZERO_FP16>(d, rp, n_ranks, rs.data(), m, inv_scale, ctl, ps,
-                                                pf, splits, blocks, stream)
-             : reduce_check_ranges_t<ZERO_BF16>(d, rp, n_ranks, rs.data(), m, inv_scale, ctl, ps,
-                                                pf, splits, blocks, stream);
+    const int rc = dtype == ZERO_FP16
+                       ? reduce_check_ranges_t<ZERO_FP16>(d, rps, n_ranks, rs.data(), m, inv_scale,
+                                                          ctl, ps, pf, splits, blocks, stream)
+                       : reduce_check_ranges_t<ZERO_BF16>(d, rps, n_ranks, rs.data(), m, inv_scale,
+                                                          ctl, ps, pf, splits, blocks, stream);
     if (rc != ZERO_OK) return rc;
     return fold_into(ws, L, inv_scale, ctl, accumulate, res, stream);
+}
+
+int reduce_check_ranges_impl(void* dst, const void* const* srcs, int32_t n_ranks,
+                             const zero_range* ranges, int32_t n, int32_t dtype, float inv_scale,
+                             const zero_step_control* ctl, zero_step_result* res, void* workspace,
+                             size_t workspace_bytes, int32_t accumulate, hipStream_t stream) {
+    int rc = reduce_list_args(n_ranks, dtype, srcs, inv_scale, res, workspace);
+    if (rc != ZERO_OK) return rc;
+    bool any = false;
+    rc = check_ranges(ranges, n, &any);
+    if (rc != ZERO_OK) return rc;
+    if (any && !dst) return ZERO_EINVAL;
+    RankPtrs rp;
+    for (int r = 0; r < ZERO_MAX_RANKS; ++r) rp.p[r] = nullptr;
+    for (int r = 0; r < n_ranks; ++r) {
+        if (any && !srcs[r]) return ZERO_EINVAL;
+        rp.p[r] = (const uint16_t*)srcs[r];
+    }
+    if (workspace_bytes < levels_for(ranges_max_blocks(ranges, n)).bytes) return ZERO_EINVAL;
+    // empty ranges take no blocks and touching ones are merged (with no
+    // elements at all only the result is written, or left as it is when
+    // accumulating); the workspace bound above holds for the merged list
+    const std::vector<zero_range> rs = merged_ranges(ranges, n);
+    std::vector<RankPtrs> rps;
+    for (const zero_range& rg : rs) {
+        RankPtrs sr = rp;
+        for (int k = 0; k < n_ranks; ++k) sr.p[k] = rp.p[k] + rg.offset;
+        rps.push_back(sr);
+    }
+    return reduce_check_list((uint16_t*)dst, rps, rs, n_ranks, dtype, inv_scale, ctl, res,
+                             workspace, accumulate, stream);
+}
+
+int reduce_check_buckets_impl(void* dst, const void* const* srcs, int32_t n_ranks,
+                              const zero_range* windows, int32_t n, int32_t dtype,
+                              float inv_scale, const zero_step_control* ctl,
+                              zero_step_result* res, void* workspace, size_t workspace_bytes,
+                              int32_t accumulate, hipStream_t stream) {
+    int rc = reduce_list_args(n_ranks, dtype, srcs, inv_scale, res, workspace);
+    if (rc != ZERO_OK) return rc;
+    bool any = false;
+    rc = check_ranges(windows, n, &any);
+    if (rc != ZERO_OK) return rc;
+    if (any && !dst) return ZERO_EINVAL;
+    if (workspace_bytes < levels_for(ranges_max_blocks(windows, n)).bytes) return ZERO_EINVAL;
+    // every non-empty window in list order, each with its own rank buffers
+    std::vector<zero_range> rs;
+    std::vector<RankPtrs> rps;
+    for (int32_t w = 0; w < n; ++w) {
+        if (windows[w].count == 0) continue;
+        RankPtrs sr;
+        for (int r = 0; r < ZERO_MAX_RANKS; ++r) sr.p[r] = nullptr;
+        for (int r = 0; r < n_ranks; ++r) {
+            const void* p = srcs[(size_t)w * n_ranks + r];
+            if (!p) return ZERO_EINVAL;
+            sr.p[r] = (const uint16_t*)p;
+        }
+        rs.push_back(windows[w]);
+        rps.push_back(sr);
+    }
+    return reduce_check_list((uint16_t*)dst, rps, rs, n_ranks, dtype, inv_scale, ctl, res,
+                             workspace, accumulate, stream);
 }
 
 template <int DT>
@@ -1081,6 +1255,16 @@ int zero_reduce_check_ranges(void* dst, const void* const* srcs, int32_t n_ranks
     return reduce_check_ranges_impl(dst, srcs, n_ranks, ranges, n_ranges, dtype,
                                     ctl ? 1.0f : inv_scale, ctl, res, workspace, workspace_bytes,
                                     accumulate, stream);
+}
+
+int zero_reduce_check_buckets(void* dst, const void* const* srcs, int32_t n_ranks,
+                              const zero_range* windows, int32_t n_windows, int32_t dtype,
+                              float inv_scale, const zero_step_control* ctl,
+                              zero_step_result* res, void* workspace, size_t workspace_bytes,
+                              int32_t accumulate, hipStream_t stream) {
+    return reduce_check_buckets_impl(dst, srcs, n_ranks, windows, n_windows, dtype,
+                                     ctl ? 1.0f : inv_scale, ctl, res, workspace, workspace_bytes,
+                                     accumulate, stream);
 }
 
 int zero_adamw_step_ranges(float* master, float* exp_avg, float* exp_avg_sq, void* param16,

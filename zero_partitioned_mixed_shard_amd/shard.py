@@ -22,6 +22,18 @@ call per window and per owner.
 With fused=False the reduce and the check are separate calls
 (zero_reduce_owned per window, then zero_unscale_check_norm per owner).
 
+Rank data.  With own_ranks=True the step holds the N ranks' 16-bit
+gradients itself, in one of two layouts (`rank_layout`):
+  flat    one buffer of the step's whole range per rank (rank_bufs);
+  bucket  one block per reduce window holding that window's N rank slices
+          back to back (rank_slices[w][r]), as the owner receives them bucket
+          by bucket (ZeRO-2 source walkthrough section 4.2), reduced with one
+          zero_reduce_check_buckets call.  On MI355X the 8-rank reduce over
+          the LLaMA-70B shard ran at 6.42 TB/s on every base offset tried
+          with 5e8-element buckets laid out this way, against 5.98-6.40 TB/s
+          with eight whole-shard rank buffers.
+fill_ranks() and rank_element() reach the rank data in either layout.
+
 With device_control=True the loss scaler and the step count live on the
 device (zero_step_control): the step runs the *_ctl calls and ends with
 zero_step_control_update, so it needs no host round trip and can be
@@ -38,9 +50,13 @@ allocation, in one of the orders of ARENA_ORDERS (`placement`):
   rank_block_b  master, m, 16-bit copy, rank buffers, reduced gradient, v;
   master_ranks  master, rank buffers, reduced gradient, m, v, 16-bit copy;
   streams_first the AdamW arrays, then the rank buffers;
-  ranks_first   the rank buffers, then the AdamW arrays.
-`min_gap` bytes additionally puts each AdamW array at least that far from the
-previous one.  On MI355X the HBM bandwidth of both passes depends on where
+  ranks_first   the rank buffers, then the AdamW arrays;
+  spread        master, the rank data, the reduced gradient and the 16-bit
+                copy, then m and v.
+`min_gap` bytes additionally keeps the bases of master, m and v at least
+that far apart (halved, down to 0, where the device cannot hold the arena):
+over the LLaMA-7B shard AdamW ran at 6.3-6.4 TB/s with them 32 GiB apart in
+every order, against 5.9-6.0 TB/s packed.  On MI355X the HBM bandwidth of both passes depends on where
 the arrays sit in physical memory, which a process cannot see: the same
 buffers at the same offsets run at different rates in arenas of different
 sizes, and shifting the LLaMA-7B shard's whole layout by 4 GiB steps moves
@@ -59,6 +75,7 @@ Nothing here computes on the data; it sequences calls and keeps host scalars.
 """
 from __future__ import annotations
 
+import re
 from dataclasses import dataclass
 from typing import List, Optional, Sequence, Tuple
 
@@ -71,7 +88,7 @@ from . import (RESULT_BYTES, ZERO_BF16, ZERO_FP16, control_to_device, read_contr
                zero_loss_scaler_update, zero_reduce_check_owned, zero_reduce_check_owned_ctl,
                zero_reduce_owned, zero_step_control_init, zero_step_control_update,
                zero_unscale_check_norm, zero_unscale_check_norm_ctl, zero_adamw_step_ranges,
-               zero_range_workspace_bytes, zero_reduce_check_ranges)
+               zero_range_workspace_bytes, zero_reduce_check_buckets, zero_reduce_check_ranges)
 
 
 def _interleaved(names, streams, in_place):
@@ -99,7 +116,9 @@ def _rank_block(head):
 
 
 def _rank_names(names):
-    return sorted((nm for nm in names if nm.startswith("rank")), key=lambda x: int(x[4:]))
+    """The rank-data buffers (one per rank, or one per reduce window) in order."""
+    return sorted((nm for nm in names if nm.startswith("rank")),
+                  key=lambda x: int(re.search(r"\d+$", x).group()))
 
 
 def _streams_first(names, streams, in_place):
@@ -112,9 +131,25 @@ def _ranks_first(names, streams, in_place):
     return _rank_names(names) + [nm for nm in names if not nm.startswith("rank")]
 
 
+def _spread(names, streams, in_place):
+    """master, the rank data, the reduced gradient and the 16-bit copy, then
+    m and v (with a min_gap, the space between master and m holds the rank
+    data)."""
+    head = [nm for nm in ("master",) if nm in names]
+    mid = [nm for nm in ("red", "param16") if nm in names]
+    tail = [nm for nm in ("exp_avg", "exp_avg_sq") if nm in names]
+    return head + _rank_names(names) + mid + tail
+
+
 # Spacing of the base offsets at which a measured placement tries each
 # order inside the arena's slack.
 PLACEMENT_STEP = 4 << 30
+
+# The arrays a min_gap keeps apart: AdamW's fp32 state.  On MI355X AdamW over
+# a LLaMA-7B-sized shard ran at 6.22-6.41 TB/s with master, m and v 24-48 GiB
+# apart at any base offset tried, against 5.5-6.0 TB/s with them 3-12 GiB
+# apart (most bases); the reduce's rank data ran fastest packed together.
+FP32_ARRAYS = ("master", "exp_avg", "exp_avg_sq")
 
 # Buffer orders an arena can be laid out in (see the module docstring).
 ARENA_ORDERS = {
@@ -124,6 +159,7 @@ ARENA_ORDERS = {
     "master_ranks": _rank_block(["master"]),
     "streams_first": _streams_first,
     "ranks_first": _ranks_first,
+    "spread": _spread,
 }
 
 
@@ -145,7 +181,8 @@ class ShardStep:
                  divisor: int = 1, in_place_rank: Optional[int] = None, fused: bool = True,
                  own_ranks: bool = False, world: int = 0, arena: bool = False,
                  min_gap: int = 0, device_control: bool = False, placement: str = "interleaved",
-                 arena_slack: int = 0, batched: bool = True, device="cuda"):
+                 arena_slack: int = 0, batched: bool = True, rank_layout: str = "flat",
+                 device="cuda"):
         self.begin, self.end = begin, end
         self.count = end - begin
         self.owners = [(a - begin, b - begin) for a, b in owners]
@@ -173,6 +210,12 @@ class ShardStep:
             raise ValueError("own_ranks needs world >= 1")
         if placement != "auto" and placement not in ARENA_ORDERS:
             raise ValueError(f"placement: one of {sorted(ARENA_ORDERS)} or 'auto'")
+        if rank_layout not in ("flat", "bucket"):
+            raise ValueError("rank_layout: 'flat' or 'bucket'")
+        if rank_layout == "bucket" and (not own_ranks or in_place_rank is not None or not fused):
+            raise ValueError("the bucket rank layout needs own_ranks, a reduced buffer of its own "
+                             "and the fused reduce+check")
+        self.rank_layout = rank_layout
         self.n_ranks = n_ranks
         self.res = torch.zeros(RESULT_BYTES // 4, dtype=torch.int32, device=device)
         self.ctl = None
@@ -183,13 +226,14 @@ class ShardStep:
         self._owner_list = [(a, b - a) for a, b in self.owners]
         spans = [b - a for a, b in self.owners] + [b - a for a, b in self.reduce_ranges]
         ws = max(zero_check_workspace_bytes(n) for n in spans) if spans else 64
-        if batched and len(self._reduce_list) > 1:
+        if batched and (len(self._reduce_list) > 1 or rank_layout == "bucket"):
             ws = max(ws, zero_range_workspace_bytes(self._reduce_list))
         self.workspace = torch.empty((ws + 7) // 8, dtype=torch.float64, device=device)
         self.placement = placement if arena else "separate"
         self.placement_ms = {}                  # first stage: one timed step per candidate
         self.placement_finalists_ms = {}        # second stage: median of three, six fastest
         self.arena_slack = 0
+        self.fp32_gap = 0                       # distance kept between master, m and v
         self._allocate(n, n_ranks, in_place_rank is None, arena, min_gap, placement,
                        arena_slack, device)
         self.exp_avg.zero_()
@@ -200,34 +244,59 @@ class ShardStep:
 
     # ----------------------------------------------------------- placement
     def _allocate(self, n, n_ranks, separate_red, arena, min_gap, placement, slack, device):
-        f32, b16 = (torch.float32, 4), (self.tdtype, 2)
-        streams = [("master", f32), ("exp_avg", f32), ("exp_avg_sq", f32), ("param16", b16)]
-        ranks = [(f"rank{r}", b16) for r in range(n_ranks)]
+        f32, b16 = torch.float32, self.tdtype
+        # name -> (dtype, elements)
+        streams = {"master": (f32, n), "exp_avg": (f32, n), "exp_avg_sq": (f32, n),
+                   "param16": (b16, n)}
         if separate_red:
-            streams.append(("red", b16))
+            streams["red"] = (b16, n)
+        ranks = {}
+        self._rank_geom = []
+        if self.rank_layout == "bucket":
+            # one block per reduce window holding its N rank slices back to
+            # back; slice r starts at r*stride + lead, with lead = the window's
+            # offset mod 8, so that every slice has the reduced buffer's
+            # 16-byte phase at that offset (the vector path needs a common one)
+            for w, (a, b) in enumerate(self.reduce_ranges):
+                lead = a % 8
+                stride = (lead + (b - a) + 7) // 8 * 8
+                self._rank_geom.append((lead, stride))
+                ranks[f"rankw{w}"] = (b16, n_ranks * stride)
+        else:
+            for r in range(n_ranks):
+                ranks[f"rank{r}"] = (b16, n)
+        kinds = {**streams, **ranks}
         if not arena:
-            self._set_views({name: torch.empty(n, dtype=dt, device=device)
-                             for name, (dt, _) in streams + ranks})
+            self._set_views({name: torch.empty(cnt, dtype=dt, device=device)
+                             for name, (dt, cnt) in kinds.items()})
             return
-        names = [nm for nm, _ in streams + ranks]
-        kinds = dict(streams + ranks)
-        stream_set = {nm for nm, _ in streams}
+        sizes = {name: cnt * torch.tensor([], dtype=dt).element_size()
+                 for name, (dt, cnt) in kinds.items()}
+        names = list(kinds)
+        stream_set = set(streams)
         if self.in_place_rank is not None and self.in_place_rank < n_ranks:
             # the reduced gradient lives in the owner's own rank buffer: an AdamW stream
             stream_set.add(f"rank{self.in_place_rank}")
+        free, _ = torch.cuda.mem_get_info(device)
         orders = ARENA_ORDERS if placement == "auto" else {placement: ARENA_ORDERS[placement]}
         plans = {}
+        gaps = {}
         for name, order_fn in orders.items():
             seq = order_fn(names, stream_set, self.in_place_rank)
             assert sorted(seq) == sorted(names), (name, seq)
-            plans[name] = self._place(seq, kinds, stream_set, n, min_gap)
+            # the widest of min_gap, min_gap / 2, min_gap / 4 and 0 between
+            # the bases of master, m and v that leaves 4 GiB of the device free
+            for gap in (min_gap, min_gap // 2, min_gap // 4, 0):
+                plan = self._place(seq, sizes, set(FP32_ARRAYS), gap)
+                if plan[1] + (4 << 30) <= free or gap == 0:
+                    break
+            plans[name], gaps[name] = plan, gap
         size = max(end for _, end in plans.values())
         # slack: unused bytes at one end of the arena, up to what the device
         # has free (4 GiB kept back); the buffers start at the arena's start
         # or `slack` bytes in, which moves them to other physical addresses
         align = 1 << 16
         if slack > 0:
-            free, _ = torch.cuda.mem_get_info(device)
             slack = max(0, min(int(slack), free - size - (4 << 30))) // align * align
         self.arena_slack = slack
         if slack > 0:
@@ -240,41 +309,55 @@ class ShardStep:
                     plans[f"{name}@+{b / 2 ** 30:g}GiB"] = (
                         {k: v + b for k, v in offs.items()}, end + b)
         self.arena = torch.empty(max(size + slack, 1), dtype=torch.uint8, device=device)
+        self._kinds, self._sizes = kinds, sizes
         if len(plans) == 1 or n_ranks == 0:
             best = next(iter(plans))
         else:
-            best = self._tune(plans, kinds, n)
+            best = self._tune(plans)
         self.placement = best
-        self._set_views(self._carve(plans[best][0], kinds, n))
+        self.fp32_gap = gaps[best.split("@")[0]]
+        self.placement_offsets = dict(plans[best][0])
+        self._set_views(self._carve(plans[best][0]))
 
     @staticmethod
-    def _place(seq, kinds, stream_set, n, min_gap):
+    def _place(seq, sizes, gap_set, min_gap):
         """Byte offsets of the buffers laid out in `seq` order (64 KiB
-        aligned), each AdamW array at least `min_gap` after the previous one."""
+        aligned), each buffer of `gap_set` at least `min_gap` after the base
+        of the previous one; -> (offsets, end)."""
         align = 1 << 16
-        offs, cur, last_stream = {}, 0, None
+        offs, cur, last = {}, 0, None
         for name in seq:
-            is_stream = name in stream_set
-            if is_stream and last_stream is not None:
-                cur = max(cur, last_stream + min_gap)
+            gapped = name in gap_set
+            if gapped and last is not None:
+                cur = max(cur, last + min_gap)
             cur = (cur + align - 1) // align * align
             offs[name] = cur
-            if is_stream:
-                last_stream = cur
-            cur += n * kinds[name][1]
+            if gapped:
+                last = cur
+            cur += sizes[name]
         return offs, cur
 
-    def _carve(self, offs, kinds, n):
-        return {name: self.arena[o:o + n * kinds[name][1]].view(kinds[name][0])
+    def _carve(self, offs):
+        return {name: self.arena[o:o + self._sizes[name]].view(self._kinds[name][0])
                 for name, o in offs.items()}
 
     def _set_views(self, bufs):
         self.master, self.exp_avg, self.exp_avg_sq = bufs["master"], bufs["exp_avg"], bufs["exp_avg_sq"]
         self.param16 = bufs["param16"]
         self.red = bufs.get("red")
-        self.rank_bufs = [bufs[f"rank{r}"] for r in range(self.n_ranks)]
+        if self.rank_layout == "bucket":
+            self.rank_bufs = None
+            self.rank_slices = []
+            for w, (a, b) in enumerate(self.reduce_ranges):
+                blk = bufs[f"rankw{w}"]
+                lead, stride = self._rank_geom[w]
+                self.rank_slices.append([blk[r * stride + lead:r * stride + lead + (b - a)]
+                                         for r in range(self.n_ranks)])
+        else:
+            self.rank_bufs = [bufs[f"rank{r}"] for r in range(self.n_ranks)]
+            self.rank_slices = None
 
-    def _tune(self, plans, kinds, n) -> str:
+    def _tune(self, plans) -> str:
         """Times the step's own calls (reduce windows, check, AdamW per owner)
         in every candidate placement on a zeroed arena and returns the
         fastest: one warm-up and one timed step each, then three more for
@@ -284,14 +367,14 @@ class ShardStep:
         same.)"""
         self.arena.zero_()
         for name, (offs, _) in plans.items():
-            self._set_views(self._carve(offs, kinds, n))
+            self._set_views(self._carve(offs))
             self.launch()
             self.placement_ms[name] = self._time_steps(1)
         # the shortest of many single samples is biased low: the finalists are
         # compared by the median of three fresh steps each
         finals = {}
         for name in sorted(self.placement_ms, key=self.placement_ms.get)[:6]:
-            self._set_views(self._carve(plans[name][0], kinds, n))
+            self._set_views(self._carve(plans[name][0]))
             self.launch()
             finals[name] = self._time_steps(3, median=True)
         self.placement_finalists_ms = finals
@@ -333,12 +416,36 @@ class ShardStep:
             rank_bufs = self.rank_bufs
         return rank_bufs[self.in_place_rank] if self.red is None else self.red
 
+    def fill_ranks(self, fill) -> None:
+        """Write the step's own rank data: fill(r, a, b, out) stores rank r's
+        gradient for shard elements [a, b) into the 16-bit tensor `out`.  It
+        is called once per rank (flat layout) or once per rank and reduce
+        window (bucket layout)."""
+        if self.rank_layout == "bucket":
+            for w, (a, b) in enumerate(self.reduce_ranges):
+                for r in range(self.n_ranks):
+                    fill(r, a, b, self.rank_slices[w][r])
+        else:
+            for r, buf in enumerate(self.rank_bufs):
+                fill(r, 0, self.count, buf)
+
+    def rank_element(self, r: int, i: int) -> torch.Tensor:
+        """One-element view of rank r's gradient at shard element i (which must
+        lie in a reduce window under the bucket layout)."""
+        if self.rank_layout == "bucket":
+            for w, (a, b) in enumerate(self.reduce_ranges):
+                if a <= i < b:
+                    return self.rank_slices[w][r][i - a:i - a + 1]
+            raise IndexError(f"element {i} lies in no reduce window")
+        return self.rank_bufs[r][i:i + 1]
+
     def launch(self, rank_bufs: Optional[Sequence[torch.Tensor]] = None,
                marks: Optional[List] = None) -> None:
         """Enqueue reduce -> check -> AdamW on the current stream (and, with
         device control, the control update).  `marks` (4 events) are recorded
         before reduce, check, AdamW and after.  Without rank_bufs the step's
         own rank buffers are used."""
+        bucket = rank_bufs is None and self.rank_layout == "bucket"
         if rank_bufs is None:
             rank_bufs = self.rank_bufs
         red = self.reduced(rank_bufs)
@@ -346,7 +453,24 @@ class ShardStep:
         inv = self.inv_scale
         if marks:
             marks[0].record()
-        if self.fused and self.batched and len(self._reduce_list) > 1:
+        if bucket and self.batched:
+            # every window's own rank slices, one call, one fold of the norm
+            zero_reduce_check_buckets(red, self._reduce_list, self.rank_slices, inv, self.res,
+                                      self.workspace, ctl_dev=ctl)
+            if marks:
+                marks[1].record()
+        elif bucket:
+            for k, (a, b) in enumerate(self.reduce_ranges):
+                srcs = self.rank_slices[k]
+                if ctl is None:
+                    zero_reduce_check_owned(red[a:b], srcs, inv, self.res, self.workspace,
+                                            accumulate=k > 0)
+                else:
+                    zero_reduce_check_owned_ctl(red[a:b], srcs, ctl, self.res, self.workspace,
+                                                accumulate=k > 0)
+            if marks:
+                marks[1].record()
+        elif self.fused and self.batched and len(self._reduce_list) > 1:
             zero_reduce_check_ranges(red, rank_bufs, self._reduce_list, inv, self.res,
                                      self.workspace, ctl_dev=ctl)
             if marks:
