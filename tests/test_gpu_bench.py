@@ -1,8 +1,8 @@
 """bench.py end to end on the GPU, on the small shards: one JSON line with
 the fields of its contract, whole steps counted, the roofline entry present,
-and the measured placement reported (device-resident and host step control,
-and the inf/NaN protocol of the fragmented-bucket workload); and the smoke()
-entry point."""
+the fixed placement or the measured one reported, a secondary shard
+(device-resident and host step control, and the inf/NaN protocol of the
+fragmented-bucket workload); and the smoke() entry point."""
 import json
 import os
 import subprocess
@@ -41,8 +41,23 @@ def test_toy_json_line(control):
     assert r["achieved"] == pytest.approx(b["phases"][dom]["bytes_per_elem"]
                                           * b["config"]["owned_elems"]
                                           / (b["phases"][dom]["ms"] * 1e-3) / 1e9, rel=1e-3)
-    assert b["config"]["placement_setup_ms"] and "buffer order" in b["config"]["placement"]
+    # the fixed default order, no placement search
+    assert "buffer order ranks_first" in b["config"]["placement"]
+    assert b["config"]["placement_search"] is False and b["config"]["placement_setup_ms"] is None
     assert b["final_norm"] is not None and b["final_norm"] > 0
+
+
+def test_placement_search_and_secondary_shard():
+    """--placement auto times the orders at setup and reports the finalists;
+    --secondary times a second shard in the same run and reports it as its
+    own object with the same measured fields."""
+    b = _bench("--workload", "toy", "--steps", "3", "--warmup", "1", "--placement", "auto",
+               "--secondary", "bert", "--secondary-steps", "3")
+    assert b["config"]["placement_search"] is True and b["config"]["placement_setup_ms"]
+    s = b["secondary"]
+    assert s["workload"].startswith("bert") and s["steps"] == 3 and s["applied_steps"] == 3
+    assert s["value"] > 0 and 0 < s["step_frac_of_peak"] < 1
+    assert s["roofline"]["bound"] == "hbm" and s["config"]["owned_elems"] == 13_685_280
 
 
 def test_buckets_overflow_protocol():
