@@ -261,6 +261,26 @@ int zero_reduce_check_owned(void* dst, const void* const* srcs, int32_t n_ranks,
                             void* workspace, size_t workspace_bytes, int32_t accumulate,
                             hipStream_t stream);
 
+/* zero_reduce_check_owned without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the check partials live in a
+ * scratch array inside the library, one per device, allocated when the
+ * library's code is loaded on that device and held until the process ends
+ * (24 MiB).  The call itself allocates nothing.  Same arguments and result as
+ * zero_reduce_check_owned.
+ *   count  at most 2^32 elements; a larger count returns ZERO_ERANGE and
+ *          launches nothing
+ * Every call on a device shares that device's scratch array: calls that can
+ * overlap on one device (on different streams, or from several host threads
+ * without ordering) race and give wrong results.  The array needs no
+ * clearing: each call writes every partial it reads.  ZERO_EDEVICE if the
+ * device of `stream` (the current device for the null stream) cannot be
+ * queried. */
+int zero_reduce_check_owned_noalloc(void* dst, const void* const* srcs, int32_t n_ranks,
+                                    int64_t count, int32_t dtype, float inv_scale,
+                                    zero_step_result* res, int32_t accumulate,
+                                    hipStream_t stream);
+
 /* Bytes of device workspace that zero_unscale_check_norm and
  * zero_reduce_check_owned need for `count` elements: one 12-byte partial per
  * 2048 elements plus the fold levels (about count / 170 bytes; 50.6 MB for

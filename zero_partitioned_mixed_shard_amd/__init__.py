@@ -65,7 +65,7 @@ EXPORTS = (
     "zero_step_control_init", "zero_reduce_check_owned_ctl", "zero_unscale_check_norm_ctl",
     "zero_adamw_step_ctl", "zero_step_control_update",
     "zero_range_workspace_bytes", "zero_reduce_check_ranges", "zero_adamw_step_ranges",
-    "zero_reduce_check_buckets",
+    "zero_reduce_check_buckets", "zero_reduce_check_owned_noalloc",
 )
 
 
@@ -122,6 +122,7 @@ def _load():
         "zero_adamw_step_ranges": ([P, P, P, P, P, P, i32, i32, P, P, P, P], ctypes.c_int),
         "zero_reduce_check_buckets": ([P, P, i32, P, i32, i32, f32, P, P, P, ctypes.c_size_t, i32,
                                        P], ctypes.c_int),
+        "zero_reduce_check_owned_noalloc": ([P, P, i32, i64, i32, f32, P, i32, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -503,3 +504,24 @@ def zero_reduce_check_buckets(dst, windows: Sequence, srcs: Sequence[Sequence], 
         float(inv_scale), _ctl(ctl_dev) if ctl_dev is not None else None, res.data_ptr(),
         _dev(workspace, workspace.element_size(), 0, "workspace"), ws_bytes,
         int(bool(accumulate)), _stream(stream)), "zero_reduce_check_buckets")
+
+
+def zero_reduce_check_owned_noalloc(dst, srcs: Sequence, inv_scale: float, res,
+                                    accumulate: bool = False, count: Optional[int] = None,
+                                    stream=None) -> None:
+    """zero_reduce_check_owned with the library's own per-device scratch
+    array instead of a workspace (nothing is allocated by the call)."""
+    count = dst.numel() if count is None else count
+    dt = _dtype_code(dst)
+    if not 1 <= len(srcs) <= ZERO_MAX_RANKS:
+        raise ValueError("1..16 rank buffers")
+    for s in srcs:
+        if _dtype_code(s) != dt:
+            raise TypeError("rank buffers and dst must share the 16-bit type")
+    if not res.is_cuda or res.numel() * res.element_size() < RESULT_BYTES:
+        raise ValueError("res must be a device tensor of at least 16 bytes")
+    ptrs = (ctypes.c_void_p * len(srcs))(*[_dev(s, 2, count, "src") for s in srcs])
+    _check(_lib.zero_reduce_check_owned_noalloc(_dev(dst, 2, count, "dst"), ptrs, len(srcs), count,
+                                                dt, float(inv_scale), res.data_ptr(),
+                                                int(bool(accumulate)), _stream(stream)),
+           "zero_reduce_check_owned_noalloc")

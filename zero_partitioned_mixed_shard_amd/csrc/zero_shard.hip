@@ -42,6 +42,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -1062,6 +1063,61 @@ int adamw_ranges_impl(float* master, float* exp_avg, float* exp_avg_sq, void* pa
 
 }  // namespace
 
+// ------------------------------------------------ allocation-free variant --
+// zero_reduce_check_owned_noalloc keeps the check partials (the workspace of
+// the other calls) in `scratch`, one copy per device for the life of the
+// process, so that callers that cannot allocate need no workspace.  It takes
+// up to kNoAllocMaxCount elements; kScratchBytes is the workspace that count
+// needs (24 MiB).
+namespace {
+constexpr int64_t kNoAllocMaxCount = int64_t(1) << 32;
+
+constexpr size_t workspace_bound(int64_t blocks) {
+    size_t off = 0;
+    int64_t n = blocks;
+    while (true) {
+        off += (size_t)n * sizeof(double);
+        off += ((size_t)n * sizeof(uint32_t) + 7) & ~(size_t)7;
+        if (n <= kFinal) break;
+        n = (n + kFold - 1) / kFold;
+    }
+    return off;
+}
+constexpr size_t kScratchBytes =
+    (workspace_bound((kNoAllocMaxCount + kTile - 1) / kTile + 1) + 255) / 256 * 256;
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device
+
+// The device address of `scratch` on the device that runs `stream` (the
+// current device for the null stream), looked up once per device with that
+// device current.
+int scratch_for_stream(hipStream_t stream, void** out) {
+    int dev = 0;
+    if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+        return ZERO_EDEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return ZERO_EDEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return ZERO_EDEVICE;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return ZERO_EDEVICE;
+        void* p = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return ZERO_EDEVICE;
+        if (err != hipSuccess || !p) return ZERO_EDEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ZERO_OK;
+}
+}  // namespace
+
 // ================================================================ C ABI =====
 extern "C" {
 
@@ -1212,6 +1268,19 @@ int zero_reduce_check_owned(void* dst, const void* const* srcs, int32_t n_ranks,
                             size_t workspace_bytes, int32_t accumulate, hipStream_t stream) {
     return reduce_check_impl(dst, srcs, n_ranks, count, dtype, inv_scale, nullptr, res, workspace,
                              workspace_bytes, accumulate, stream);
+}
+
+int zero_reduce_check_owned_noalloc(void* dst, const void* const* srcs, int32_t n_ranks,
+                                    int64_t count, int32_t dtype, float inv_scale,
+                                    zero_step_result* res, int32_t accumulate,
+                                    hipStream_t stream) {
+    if (count < 0) return ZERO_EINVAL;
+    if (count > kNoAllocMaxCount) return ZERO_ERANGE;
+    void* ws = nullptr;
+    const int rc = scratch_for_stream(stream, &ws);
+    if (rc != ZERO_OK) return rc;
+    return reduce_check_impl(dst, srcs, n_ranks, count, dtype, inv_scale, nullptr, res, ws,
+                             kScratchBytes, accumulate, stream);
 }
 
 int zero_reduce_check_owned_ctl(void* dst, const void* const* srcs, int32_t n_ranks,
