@@ -21,8 +21,11 @@ buckets; each bucket's 8 slices back to back), and the buffers sit in one
 arena in a fixed order (ranks_first, master / m / v at least 32 GiB apart):
 no placement search unless --placement auto.  After the 70B shard is freed
 the LLaMA-7B-shaped shard (842,301,952 owned elements) is timed the same way
-and reported as the "secondary" object (--secondary none skips it;
---workload llama7b runs it alone).
+and reported as the "secondary" object, then once more with its placement
+measured at setup ("secondary_tuned": every arena order at base offsets 4 GiB
+apart in 64 GiB of slack; the 7B shard's rate follows the physical addresses
+its arrays land on, which vary between allocations and boxes).
+--secondary none skips both; --workload llama7b runs the 7B shard alone.
 
 Prints one JSON line: params updated per second (owned elements x applied
 steps / time), per-phase times measured with HIP events on the stream the
@@ -47,7 +50,7 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SRCS = [os.path.join(ROOT, "zero_partitioned_mixed_shard_amd", "csrc", f)
                for f in ("zero_common.h", "zero_shard.hip")]
 COUNTERS = {w: os.path.join(ROOT, "profiles", f"adamw_reduce_{w}_hbm_counters.md")
-            for w in ("toy", "bert", "llama7b", "llama70b")}
+            for w in ("toy", "bert", "llama7b", "llama70b", "buckets")}
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -103,6 +106,9 @@ def parse():
                          "reported as the 'secondary' object (default: llama7b after llama70b; "
                          "'none' to skip)")
     ap.add_argument("--secondary-steps", type=int, default=20)
+    ap.add_argument("--no-secondary-tuned", action="store_true",
+                    help="skip the secondary shard's second run with its placement measured at "
+                         "setup ('secondary_tuned')")
     ap.add_argument("--arena-slack-gib", type=float, default=0.0,
                     help="allocate the arena up to this much larger (never more than is free, "
                          "less 4 GiB) and let --placement auto also try every order at base "
@@ -296,9 +302,14 @@ def build_buckets(wl, arena: bool = True, min_gap: int = 0, fused: bool = True,
     shard.load_param16(I.device_param16(wl, offs, 0, padded, out=shard.param16))
     for r, buf in enumerate(shard.rank_bufs):
         I.device_rank_grad(wl, 1, wl.scale0, r, 0, padded, padded, out=buf)
-    # rank 0's gradient as per-parameter tensors holding the same values
+    # rank 0's gradient as per-parameter tensors (one allocation each) holding
+    # the same values, written by the seeded generator straight into each
+    # tensor: the setup makes no device-to-device copies
     flat0 = shard.rank_bufs[0]
-    grads = [flat0[int(o):int(o) + int(n)].clone() for o, n in zip(offs, wl.numels)]
+    grads = []
+    for o, n in zip(offs, wl.numels):
+        o, n = int(o), int(n)
+        grads.append(I.device_rank_grad(wl, 1, wl.scale0, 0, o, o + n, padded))
     flat0.fill_(-1.0)                       # the copy-in must rewrite every element
     tables = []
     for b, (a, z) in enumerate(windows):
@@ -445,7 +456,22 @@ def run_workload(args, workload: str, steps: int, inject_every: int,
         one_step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    # the values the inf/NaN injections overwrite, read before the timed steps
+    originals = {}
+    for k in range(steps):
+        if inject_every and (k + 1) % inject_every == 0:
+            r = 1 + (k % (shard.n_ranks - 1)) if shard.n_ranks > 1 else 0
+            originals[k] = float(shard.rank_element(r, (k * 2654435761 + 12345) % count).item())
+    # per step, only the events the phases need (each recorded event costs a
+    # few microseconds of the step): [0] before the reduce, [1] before the
+    # separate check (--unfused), [2] before AdamW, [3] after AdamW, [4]
+    # before the copy-in, [5] after the write-back
+    def events():
+        need = {0, 2, 3} | ({1} if args.unfused else set()) | ({4} if copy_in else set()) \
+            | ({5} if write_back else set())
+        return [torch.cuda.Event(enable_timing=True) if i in need else None for i in range(6)]
+
+    ev = [events() for _ in range(steps)]
     applied = 0
     infos = []
     last_sumsq = None
@@ -472,29 +498,31 @@ def run_workload(args, workload: str, steps: int, inject_every: int,
             flush.fill_(float(k))                  # evicts the caches; outside the step's events
         planted = None
         if inject_every and (k + 1) % inject_every == 0:
-            # a rank whose data the copy-in does not rewrite; seeded index
+            # a rank whose data the copy-in does not rewrite; seeded index.
+            # After the step a fill restores the element (no device-to-device
+            # copy)
             injections += 1
             r = 1 + (k % (shard.n_ranks - 1)) if shard.n_ranks > 1 else 0
             idx = (k * 2654435761 + 12345) % count
             bad = float("inf") if injections % 2 else float("nan")
             cell = shard.rank_element(r, idx)
-            planted = (cell, cell.clone())
+            planted = (cell, originals[k])
             cell.fill_(bad)
         if graph is not None:
             ev[k][0].record()
             graph.replay()
             ev[k][3].record()
         else:
-            ev[k][4].record()
             if copy_in:
+                ev[k][4].record()
                 copy_in()
             info = one_step(marks=ev[k])
             if info is not None:
                 applied += info.applied
                 infos.append(info)
         if planted is not None:
-            cell, old = planted
-            cell.copy_(old)
+            cell, value = planted
+            cell.fill_(value)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -680,18 +708,29 @@ def main():
     }
     result.update(run)
     if args.secondary and args.secondary != args.workload:
-        # a second shard in the same run, same options, its own JSON object
-        sec = run_workload(args, args.secondary, args.secondary_steps, 0)
-        sec.pop("_begin")
+        # a second shard in the same run, same options, its own JSON object;
+        # then the same shard with its placement measured at setup (every
+        # arena order at base offsets 4 GiB apart in 64 GiB of slack), which
+        # finds physical addresses that suit it on the box at hand
         keep = ("value", "ms_per_step", "median_step_ms", "step_GBps", "step_frac_of_peak",
                 "phases", "roofline", "applied_steps", "final_norm", "per_step_ms")
-        result["secondary"] = {"workload": sec["config"]["workload"],
-                               "steps": args.secondary_steps, "unit": "params/s",
-                               **{k: sec[k] for k in keep},
-                               "config": {k: sec["config"][k] for k in
-                                          ("description", "owned_elems", "ranks", "placement",
-                                           "rank_layout", "reduce_windows", "in_place_reduce",
-                                           "placement_search", "arena_slack_gib")}}
+
+        def entry(sec):
+            sec.pop("_begin")
+            return {"workload": sec["config"]["workload"], "steps": args.secondary_steps,
+                    "unit": "params/s", **{k: sec[k] for k in keep},
+                    "config": {k: sec["config"][k] for k in
+                               ("description", "owned_elems", "ranks", "placement", "rank_layout",
+                                "reduce_windows", "in_place_reduce", "placement_search",
+                                "placement_candidates", "arena_slack_gib")}}
+
+        result["secondary"] = entry(run_workload(args, args.secondary, args.secondary_steps, 0))
+        if not args.no_secondary_tuned and args.placement != "auto":
+            fixed = (args.placement, args.arena_slack_gib)
+            args.placement, args.arena_slack_gib = "auto", 64.0
+            result["secondary_tuned"] = entry(run_workload(args, args.secondary,
+                                                           args.secondary_steps, 0))
+            args.placement, args.arena_slack_gib = fixed
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W.WORKLOADS[args.workload], begin, args.cpu_seconds)
     print(json.dumps(result), flush=True)

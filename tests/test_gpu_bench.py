@@ -58,6 +58,14 @@ def test_placement_search_and_secondary_shard():
     assert s["workload"].startswith("bert") and s["steps"] == 3 and s["applied_steps"] == 3
     assert s["value"] > 0 and 0 < s["step_frac_of_peak"] < 1
     assert s["roofline"]["bound"] == "hbm" and s["config"]["owned_elems"] == 13_685_280
+    assert "secondary_tuned" not in b           # the primary already searched
+    # fixed placement: the secondary is also run with its placement measured
+    c = _bench("--workload", "toy", "--steps", "3", "--warmup", "1", "--secondary", "bert",
+               "--secondary-steps", "3")
+    assert c["secondary"]["config"]["placement_search"] is False
+    t = c["secondary_tuned"]
+    assert t["config"]["placement_search"] is True and t["config"]["placement_candidates"] > 1
+    assert t["applied_steps"] == 3 and t["config"]["arena_slack_gib"] > 0
 
 
 def test_buckets_overflow_protocol():

@@ -442,55 +442,42 @@ class ShardStep:
     def launch(self, rank_bufs: Optional[Sequence[torch.Tensor]] = None,
                marks: Optional[List] = None) -> None:
         """Enqueue reduce -> check -> AdamW on the current stream (and, with
-        device control, the control update).  `marks` (4 events) are recorded
-        before reduce, check, AdamW and after.  Without rank_bufs the step's
-        own rank buffers are used."""
+        device control, the control update).  `marks` (4 events, any of them
+        None) are recorded before the reduce, before the separate check
+        (fused=False only), before AdamW and after AdamW (before the control
+        update).  Without rank_bufs the step's own rank data are used."""
+
+        def mark(i):
+            if marks and marks[i] is not None:
+                marks[i].record()
+
         bucket = rank_bufs is None and self.rank_layout == "bucket"
         if rank_bufs is None:
             rank_bufs = self.rank_bufs
         red = self.reduced(rank_bufs)
         ctl = self.ctl
         inv = self.inv_scale
-        if marks:
-            marks[0].record()
+        mark(0)
         if bucket and self.batched:
             # every window's own rank slices, one call, one fold of the norm
             zero_reduce_check_buckets(red, self._reduce_list, self.rank_slices, inv, self.res,
                                       self.workspace, ctl_dev=ctl)
-            if marks:
-                marks[1].record()
-        elif bucket:
-            for k, (a, b) in enumerate(self.reduce_ranges):
-                srcs = self.rank_slices[k]
-                if ctl is None:
-                    zero_reduce_check_owned(red[a:b], srcs, inv, self.res, self.workspace,
-                                            accumulate=k > 0)
-                else:
-                    zero_reduce_check_owned_ctl(red[a:b], srcs, ctl, self.res, self.workspace,
-                                                accumulate=k > 0)
-            if marks:
-                marks[1].record()
-        elif self.fused and self.batched and len(self._reduce_list) > 1:
+        elif self.fused and self.batched and not bucket and len(self._reduce_list) > 1:
             zero_reduce_check_ranges(red, rank_bufs, self._reduce_list, inv, self.res,
                                      self.workspace, ctl_dev=ctl)
-            if marks:
-                marks[1].record()
         elif self.fused:
             for k, (a, b) in enumerate(self.reduce_ranges):
-                srcs = [r[a:b] for r in rank_bufs]
+                srcs = self.rank_slices[k] if bucket else [r[a:b] for r in rank_bufs]
                 if ctl is None:
                     zero_reduce_check_owned(red[a:b], srcs, inv, self.res, self.workspace,
                                             accumulate=k > 0)
                 else:
                     zero_reduce_check_owned_ctl(red[a:b], srcs, ctl, self.res, self.workspace,
                                                 accumulate=k > 0)
-            if marks:
-                marks[1].record()
         else:
             for a, b in self.reduce_ranges:
                 zero_reduce_owned(red[a:b], [r[a:b] for r in rank_bufs])
-            if marks:
-                marks[1].record()
+            mark(1)
             for k, (a, b) in enumerate(self.owners):
                 if ctl is None:
                     zero_unscale_check_norm(red[a:b], inv, self.res, self.workspace,
@@ -498,8 +485,7 @@ class ShardStep:
                 else:
                     zero_unscale_check_norm_ctl(red[a:b], ctl, self.res, self.workspace,
                                                 accumulate=k > 0)
-        if marks:
-            marks[2].record()
+        mark(2)
         self.hp.step = self.t + 1
         if self.batched and len(self._owner_list) > 1:
             zero_adamw_step_ranges(self.master, self.exp_avg, self.exp_avg_sq, self.param16, red,
@@ -512,10 +498,9 @@ class ShardStep:
                     zero_adamw_step(*args, self.res)
                 else:
                     zero_adamw_step_ctl(*args, ctl, self.res)
+        mark(3)
         if ctl is not None:
             zero_step_control_update(ctl, self.res)
-        if marks:
-            marks[3].record()
 
     def finish(self) -> StepInfo:
         """Read the 16-byte result (synchronises) and update t and the scaler
