@@ -28,7 +28,9 @@
  *   - Buffers are flat arrays.  "device" pointers are HIP device memory owned
  *     by the caller; "host" pointers are ordinary host memory owned by the
  *     caller.  The library never allocates, frees or keeps a pointer after a
- *     call returns, and keeps no state between calls.
+ *     call returns, and keeps no state between calls, with one exception:
+ *     zero_reduce_check_owned_noalloc uses a scratch array of the library's
+ *     own, one per device, and remembers its device address.
  *   - 16-bit data (gradients, the parameter copy) is passed as raw 16-bit
  *     patterns; `dtype` says whether they are IEEE binary16 or bfloat16.
  *   - Device calls are asynchronous and ordered on `stream` (0 = the null
