@@ -106,6 +106,34 @@ def test_views_of_one_buffer(mem_gap_max):
     assert np.array_equal(to_np16(backing), want)
 
 
+def test_one_tensor_every_misalignment():
+    """One tensor spanning several blocks at every flat offset 0..7 and
+    memory offsets 0, 1 and 5 inside a larger buffer: the tensor side sits
+    0..7 elements off the flat side's 16-byte grid, so every lane, row and
+    wave edge of the copy kernels shares a misaligned chunk with the next
+    tile (within a row, from lane 63 to the next row, and across waves and
+    blocks).  The scatter must leave the buffer around the tensor untouched."""
+    rng = np.random.default_rng(77)
+    n = 3 * 8192 + 2048 + 13
+    for f in range(8):
+        for p in (0, 1, 5):
+            backing_host = rng.integers(0, 65536, n + 24).astype(np.uint16)
+            backing = torch.from_numpy(backing_host.view(np.int16)).cuda().view(torch.bfloat16)
+            t = backing[p:p + n]
+            count = f + n + 11
+            descs = Z.tensor_descs([t], [f])
+            flat = torch.full((count,), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            Z.zero_flat_gather(flat, descs)
+            want = oracle.flat_gather([backing_host[p:p + n].copy()], [f], count)
+            assert np.array_equal(to_np16(flat), want), (f, p)
+            new_flat = rng.integers(0, 65536, count).astype(np.uint16)
+            d_flat = torch.from_numpy(new_flat.view(np.int16)).cuda().view(torch.bfloat16)
+            Z.zero_flat_scatter(d_flat, descs)
+            want_b = backing_host.copy()
+            want_b[p:p + n] = oracle.flat_scatter(new_flat, [f], [n])[0]
+            assert np.array_equal(to_np16(backing), want_b), (f, p)
+
+
 def test_invalid_arguments():
     flat = torch.zeros(16, dtype=torch.bfloat16, device="cuda")
     L = Z.lib()

@@ -360,8 +360,8 @@ class ShardStep:
     def _tune(self, plans) -> str:
         """Times the step's own calls (reduce windows, check, AdamW per owner)
         in every candidate placement on a zeroed arena and returns the
-        fastest: one warm-up and one timed step each, then three more for
-        the four fastest.  Zero gradients raise no overflow, so every pass
+        fastest: one warm-up and one timed step each, then the median of
+        three more for the six fastest.  Zero gradients raise no overflow, so every pass
         runs whole.  (On MI355X a zeroed arena runs the step 0.5-1 % faster
         than gradient data, in every placement alike: the choice is the
         same.)"""
