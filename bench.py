@@ -73,6 +73,59 @@ def measured_traffic(kernel: str, workload: str):
     return int(m.group(1))
 
 
+class TimingEvent:
+    """A HIP event used only to time work on torch's current stream, created
+    with hipEventDisableSystemFence: recording it skips the system-scope
+    fence (cache write-back and invalidation) that a default event performs,
+    which on MI355X costs the stream about 5.7 us per record.  The timed
+    region's two outer events stay default torch events, and every read of
+    these follows a device synchronize.  Same record() / elapsed_time() as
+    torch.cuda.Event."""
+    FLAGS = 0x20000000                       # hipEventDisableSystemFence
+    _hip = None
+
+    @classmethod
+    def runtime(cls):
+        """The HIP runtime torch loaded (the only one in the process)."""
+        import ctypes
+        if cls._hip is None:
+            paths = [ln.split()[-1] for ln in open("/proc/self/maps")
+                     if len(ln.split()) >= 6 and "libamdhip64" in ln.split()[-1]]
+            if not paths:
+                raise RuntimeError("the HIP runtime is not loaded")
+            hip = ctypes.CDLL(paths[0])
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ev = ctypes.c_void_p()
+        if self.runtime().hipEventCreateWithFlags(ctypes.byref(self._ev), self.FLAGS) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self):
+        import torch
+        if self.runtime().hipEventRecord(self._ev, torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        if self.runtime().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self):
+        if self._ev:
+            self.runtime().hipEventDestroy(self._ev)
+            self._ev = None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +194,9 @@ def parse():
                          "a 16-byte result readback (the GPU idles while the host updates the "
                          "scaler and enqueues the next step); default: device-resident step "
                          "control, no per-step round trip")
+    ap.add_argument("--fenced-events", action="store_true",
+                    help="time the phases with default events (each record adds a system-scope "
+                         "fence, about 5.7 us of the step) instead of fence-free timing events")
     ap.add_argument("--graph", action="store_true",
                     help="keep the loss scaler and step count on the device and replay one "
                          "captured HIP graph per step (no host round trip between steps)")
@@ -462,14 +518,16 @@ def run_workload(args, workload: str, steps: int, inject_every: int,
         if inject_every and (k + 1) % inject_every == 0:
             r = 1 + (k % (shard.n_ranks - 1)) if shard.n_ranks > 1 else 0
             originals[k] = float(shard.rank_element(r, (k * 2654435761 + 12345) % count).item())
-    # per step, only the events the phases need (each recorded event costs a
-    # few microseconds of the step): [0] before the reduce, [1] before the
-    # separate check (--unfused), [2] before AdamW, [3] after AdamW, [4]
-    # before the copy-in, [5] after the write-back
+    # per step, only the events the phases need (fence-free timing events;
+    # with --fenced-events each record adds about 5.7 us to the step): [0]
+    # before the reduce, [1] before the separate check (--unfused), [2] before
+    # AdamW, [3] after AdamW, [4] before the copy-in, [5] after the write-back
     def events():
         need = {0, 2, 3} | ({1} if args.unfused else set()) | ({4} if copy_in else set()) \
             | ({5} if write_back else set())
-        return [torch.cuda.Event(enable_timing=True) if i in need else None for i in range(6)]
+        make = ((lambda: torch.cuda.Event(enable_timing=True)) if args.fenced_events
+                else TimingEvent)
+        return [make() if i in need else None for i in range(6)]
 
     ev = [events() for _ in range(steps)]
     applied = 0
@@ -633,6 +691,8 @@ def run_workload(args, workload: str, steps: int, inject_every: int,
             "step_control": "host (16-byte readback per step)" if args.host_control else
                             "device-resident (no per-step readback)",
             "graph": bool(args.graph),
+            "phase_events": ("default (system-scope fence per record)" if args.fenced_events
+                             else "fence-free timing events (hipEventDisableSystemFence)"),
             "flush_between_steps_gib": args.flush_gib,
             "inf_nan_every": inject_every,
             "placement": layout,
@@ -658,6 +718,10 @@ def run_workload(args, workload: str, steps: int, inject_every: int,
         "roofline": roofline,
         "_begin": begin,
     }
+    for e in ev:
+        for x in e:
+            if isinstance(x, TimingEvent):
+                x.destroy()
     # drop every reference to the shard's device memory before the next run
     planted = None
     del bufs, shard, flush, graph, planted, copy_in, write_back, one_step
