@@ -809,18 +809,25 @@ AdamConsts adam_consts(const zero_adamw_hparams* hp, bool ctl) {
 }
 
 // 2 resident blocks per CU: 6.10 -> 6.37 TB/s on the LLaMA-70B-shaped shard,
-// 5.33 -> 5.84 TB/s on the 7B one (MI355X)
+// 5.33 -> 5.84 TB/s on the 7B one (MI355X).  Launches of at most
+// kAdamSmallCount elements (the ToyModel and BERT-base owner shards) run 3
+// per CU: 0.059 against 0.064 ms at 1.26e7 elements, while from 2.5e7
+// elements on 2 per CU is faster.
 constexpr int kAdamBlocksPerCU = 2;
-static_assert((kThreads / 64) * kAdamWaveBytes <= kLdsPerCU / (kAdamBlocksPerCU + 1) + 2048u,
-              "the AdamW cap's dynamic LDS holds every wave's staging area");
+constexpr int kAdamSmallBlocksPerCU = 3;
+constexpr int64_t kAdamSmallCount = int64_t(1) << 24;
+static_assert((kThreads / 64) * kAdamWaveBytes <= kLdsPerCU / (kAdamSmallBlocksPerCU + 1) + 2048u,
+              "the AdamW caps' dynamic LDS holds every wave's staging area");
 
 template <int DT>
 int launch_adamw(float* master, float* exp_avg, float* exp_avg_sq, uint16_t* p16,
                  const uint16_t* g16, const Split& s, const AdamConsts& c,
                  const zero_step_control* ctl, const zero_step_result* res, hipStream_t stream) {
+    const unsigned lds = lds_for_blocks(s.count <= kAdamSmallCount ? kAdamSmallBlocksPerCU
+                                                                    : kAdamBlocksPerCU);
     return launch_pieces(s, tile_blocks(s), [&](const Split& piece, int64_t grid) {
-        return launch(adamw_kernel<DT>, grid, lds_for_blocks(kAdamBlocksPerCU), stream, master,
-                      exp_avg, exp_avg_sq, p16, g16, piece, c, ctl, res);
+        return launch(adamw_kernel<DT>, grid, lds, stream, master, exp_avg, exp_avg_sq, p16, g16,
+                      piece, c, ctl, res);
     });
 }
 
