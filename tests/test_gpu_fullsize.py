@@ -149,8 +149,9 @@ def test_llama_shard_fullsize_sampled(name, device_control):
         pytest.skip(f"{name}: needs {need / 1e9:.1f} GB of device memory, {free / 1e9:.1f} GB free")
     t0 = time.time()
     print(f"{name}: {count} owned elements, {wl.world} ranks, in_place={in_place}", flush=True)
-    # as bench.py runs it (measured placement; its arena slack moves buffers only)
-    # the layout bench.py settles on (in place where a separate buffer does not fit)
+    # as bench.py runs it: the fixed arena order, and with a reduced buffer of
+    # its own the ranks' gradients bucket by bucket (in place where a separate
+    # buffer does not fit)
     shard, _, _, _, in_place = bench.build_shard(wl, device_control=device_control,
                                                  in_place=in_place)
     bufs = shard.rank_bufs
