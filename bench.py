@@ -29,7 +29,8 @@ its arrays land on, which vary between allocations and boxes).
 
 Prints one JSON line: params updated per second (owned elements x applied
 steps / time), per-phase times measured with HIP events on the stream the
-kernels run on, the AdamW kernel's achieved HBM bandwidth against the 8 TB/s
+kernels run on (timing-only events without the system-scope fence; the two
+events around the timed steps are default ones), the AdamW kernel's achieved HBM bandwidth against the 8 TB/s
 peak, and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
