@@ -526,9 +526,15 @@ def run_workload(args, workload: str, steps: int, inject_every: int,
     def events():
         need = {0, 2, 3} | ({1} if args.unfused else set()) | ({4} if copy_in else set()) \
             | ({5} if write_back else set())
-        make = ((lambda: torch.cuda.Event(enable_timing=True)) if args.fenced_events
-                else TimingEvent)
+        make = ((lambda: torch.cuda.Event(enable_timing=True)) if fenced else TimingEvent)
         return [make() if i in need else None for i in range(6)]
+
+    fenced = args.fenced_events
+    if not fenced:
+        try:
+            TimingEvent.runtime()
+        except (OSError, RuntimeError, AttributeError):
+            fenced = True               # no handle on torch's HIP runtime: default events
 
     ev = [events() for _ in range(steps)]
     applied = 0
@@ -692,7 +698,7 @@ def run_workload(args, workload: str, steps: int, inject_every: int,
             "step_control": "host (16-byte readback per step)" if args.host_control else
                             "device-resident (no per-step readback)",
             "graph": bool(args.graph),
-            "phase_events": ("default (system-scope fence per record)" if args.fenced_events
+            "phase_events": ("default (system-scope fence per record)" if fenced
                              else "fence-free timing events (hipEventDisableSystemFence)"),
             "flush_between_steps_gib": args.flush_gib,
             "inf_nan_every": inject_every,
