@@ -268,7 +268,8 @@ int zero_reduce_check_owned(void* dst, const void* const* srcs, int32_t n_ranks,
  * loops, harnesses that forbid allocation): the check partials live in a
  * scratch array inside the library, one per device, allocated when the
  * library's code is loaded on that device and held until the process ends
- * (24 MiB).  The call itself allocates nothing.  Same arguments and result as
+ * (25,178,368 bytes, the workspace of 2^32 elements).  The call itself
+ * allocates nothing.  Same arguments and result as
  * zero_reduce_check_owned.
  *   count  at most 2^32 elements; a larger count returns ZERO_ERANGE and
  *          launches nothing

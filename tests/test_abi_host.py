@@ -308,3 +308,18 @@ def test_header_compiles_as_c(tmp_path):
     assert r.returncode == 0, r.stderr[-3000:]
     own = [l for l in r.stderr.splitlines() if "zero_shard.h:" in l and "included from" not in l]
     assert not own, own
+
+
+def test_noalloc_scratch_covers_its_largest_count():
+    """The allocation-free reduce+check keeps its check partials in an array
+    inside the library of 25,178,368 bytes (the workspace of 2^32 elements,
+    rounded up to 256 bytes) and accepts counts up to 2^32: the workspace the
+    workspace call needs for every count up to that limit fits in it, so a
+    count the call accepts is never refused for lack of scratch."""
+    limit, scratch = 1 << 32, 25_178_368
+    L = Z.lib()
+    for count in (limit, limit - 1, limit - 4095, 3 * (1 << 30) + 7, 1 << 20, 1):
+        need = L.zero_check_workspace_bytes(count)
+        assert 0 < need <= scratch, (count, need)
+    # the requirement grows with the count, so the largest count bounds them all
+    assert L.zero_check_workspace_bytes(limit) >= L.zero_check_workspace_bytes(limit // 2)
