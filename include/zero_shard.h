@@ -286,8 +286,8 @@ int zero_reduce_check_owned_noalloc(void* dst, const void* const* srcs, int32_t 
 
 /* Bytes of device workspace that zero_unscale_check_norm and
  * zero_reduce_check_owned need for `count` elements: one 12-byte partial per
- * 2048 elements plus the fold levels (about count / 170 bytes; 50.6 MB for
- * 8.6e9 elements, 64 bytes minimum). */
+ * 2048 elements plus the fold levels (about count / 170 bytes; 50.5 MB for
+ * 8.62e9 elements, 16 bytes for count 0). */
 size_t zero_check_workspace_bytes(int64_t count);
 
 /* Unscale + overflow check + squared norm over grad16[0, count):
