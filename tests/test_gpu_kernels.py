@@ -27,11 +27,14 @@ from _common import (assert_bits16_equal, assert_f32_close, assert_p16_close, fr
 pytestmark = pytest.mark.gpu
 
 FP16, BF16 = 1, 2
-COUNTS = [0, 1, 7, 8, 9, 4095, 100003]
+# 4096 and 8200: AdamW blocks of 2048 elements all whole (no register-path
+# tail at offset 0), then one lane tile past them
+COUNTS = [0, 1, 7, 8, 9, 4095, 4096, 8200, 100003]
 # the reduce takes two block-wide rows of 256 lane tiles per block (4096
 # elements): a last block with one full row and an empty second row, and one
-# whose second row holds a single lane tile
-REDUCE_COUNTS = COUNTS + [10240, 6152]
+# whose second row holds a single lane tile; 8192 and 12296: every block whole
+# (at 8 ranks all staged in LDS, at offset 0), then one lane tile past them
+REDUCE_COUNTS = COUNTS + [10240, 6152, 8192, 12296]
 SPECIAL = {FP16: [0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x7BFF, 0xFBFF, 0x7B53, 0x7C00, 0xFC00,
                   0x7E00],
            BF16: [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x7F7F, 0xFF7F, 0x7F00, 0x7F80, 0xFF80,
